@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark: F16-weight products on one MI355X, Llama-3-8B-shaped matrices.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+
+  decode (n = 1):  to_f16 of each activation column, then
+                   Q/K/V grouped GEMV, O GEMV, gate/up grouped GEMV, down GEMV
+                   and the 128256x4096 logits GEMV (vec_dot order);
+  prefill (n = 512): to_f16 of each 512-column activation block, then the
+                   exact product of every matrix (tinyBLAS order, picked by
+                   takes_sgemm) and the MFMA fp16 product of every matrix.
+
+Inputs are seeded synthetic data (N(0,0.02) f16 weights, N(0,1) f32
+activations) resident in HBM before the timed region.  The weight set is
+1.49 GB, well above the 256 MB last-level cache, so each step streams it cold.
+
+Prints ONE JSON line.  `value` is the decode GEMV throughput in GB/s
+(algorithmic bytes of the decode phase / its wall time); the n = 512 GEMM
+throughputs are reported beside it under "gemm_n512".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2516.6  # dense fp16 MFMA, 256 CUs x 2.4 GHz
+VALU_FP32_PEAK_TFLOPS = 157.3  # fp32 vector, packed FMA
+VALU_FP32_NONPACKED_TFLOPS = 78.6  # one FMA per lane per cycle: 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    p.add_argument("--cpu-sample-rows", type=int, default=16,
+                   help="the oracle's prefill sample is rows/N of every matrix")
+    return p.parse_args()
+
+
+def cpu_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_record(kernel_src: str):
+    """HBM traffic per launch measured with rocprofv3 PMC counters, read from
+    profiles/hbm_traffic.md (a fenced json block), valid only for the kernel
+    source it was measured on."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_sha") != source_hash(kernel_src):
+        return None
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (--gpus %d requested); the product shards by "
+              "output rows across GPUs, which is not built here." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import f16_weight_matrix_amd as f16wm
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    f16wm.lib()
+
+    S = dict(synth.LLAMA3_8B)
+    S["logits"] = synth.LLAMA3_8B_LOGITS
+    N = synth.PREFILL_N
+
+    t0 = time.time()
+    host_w = {m: synth.weight(synth.CFG_8B, 0, m, *S[m]) for m in S}
+    W = {m: torch.from_numpy(w.view(np.int16)).to(dev).view(torch.float16) for m, w in host_w.items()}
+    # decode activation columns (f32): attn-in, o-in, ffn-in, down-in, logits-in
+    dec = synth.activation(synth.CFG_8B, 0, 0, 5, 14336)
+    dec_k = {"attn": 4096, "o": 4096, "ffn": 4096, "down": 14336, "logits": 4096}
+    X1 = {g: torch.from_numpy(dec[i, :dec_k[g]].copy()).to(dev) for i, g in enumerate(dec_k)}
+    A1 = {g: torch.empty(dec_k[g], dtype=torch.float16, device=dev) for g in dec_k}
+    # prefill activation blocks (f32) [512][k]
+    pre = synth.activation(synth.CFG_8B_PREFILL, 0, 0, N, 14336)
+    XN = {g: torch.from_numpy(np.ascontiguousarray(pre[:, :dec_k[g]])).to(dev) for g in dec_k}
+    AN = {g: torch.empty((N, dec_k[g]), dtype=torch.float16, device=dev) for g in dec_k}
+    del pre
+    O1 = {m: torch.empty(S[m][0], dtype=torch.float32, device=dev) for m in S}
+    ON = {m: torch.empty((N, S[m][0]), dtype=torch.float32, device=dev) for m in S}
+    OM = {m: torch.empty((N, S[m][0]), dtype=torch.float32, device=dev) for m in S}
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    src_of = {"q": "attn", "k": "attn", "v": "attn", "o": "o", "gate": "ffn", "up": "ffn",
+              "down": "down", "logits": "logits"}
+    # algorithmic bytes: weight + activation (f16) + output (f32) per GEMV launch
+    gemv_launches = [("qkv", ["q", "k", "v"], "attn"), ("o", ["o"], "o"), ("gateup", ["gate", "up"], "ffn"),
+                     ("down", ["down"], "down"), ("logits", ["logits"], "logits")]
+
+    def gemv_bytes(mats, g):
+        k = dec_k[g]
+        return sum(2 * S[m][0] * k + 4 * S[m][0] for m in mats) + 2 * k
+
+    gemv_b = [gemv_bytes(ms, g) for _, ms, g in gemv_launches]
+    tof16_dec_bytes = sum(6 * k for k in dec_k.values())
+    decode_bytes = sum(gemv_b) + tof16_dec_bytes
+    flops_n512 = sum(2 * S[m][0] * S[m][1] * N for m in S)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(timed):
+        e = [ev() for _ in range(4)] if timed else None
+        ge = [(ev(), ev()) for _ in gemv_launches] if timed else None
+        if timed:
+            e[0].record()
+        # ---- decode, n = 1
+        for g in dec_k:
+            f16wm.to_f16(X1[g], A1[g])
+        for i, (name, mats, g) in enumerate(gemv_launches):
+            if timed:
+                ge[i][0].record()
+            if len(mats) > 1:
+                f16wm.mat_vec_multi([W[m] for m in mats], A1[g], [O1[m] for m in mats])
+            else:
+                f16wm.mat_vec(W[mats[0]], A1[g], O1[mats[0]])
+            if timed:
+                ge[i][1].record()
+        if timed:
+            e[1].record()
+        # ---- prefill, n = 512, exact order (takes_sgemm holds for every shape)
+        for g in dec_k:
+            f16wm.to_f16(XN[g], AN[g])
+        for m in S:
+            f16wm.mat_mul(W[m], AN[src_of[m]], ON[m])
+        if timed:
+            e[2].record()
+        # ---- prefill, n = 512, MFMA fp16
+        for m in S:
+            f16wm.mat_mul_mfma(W[m], AN[src_of[m]], OM[m])
+        if timed:
+            e[3].record()
+        return e, ge
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    recs = []
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        recs.append(step(True))
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_start
+
+    dec_ms = [e[0].elapsed_time(e[1]) for e, _ in recs]
+    exact_ms = [e[1].elapsed_time(e[2]) for e, _ in recs]
+    mfma_ms = [e[2].elapsed_time(e[3]) for e, _ in recs]
+    gemv_ms = [[a.elapsed_time(b) for a, b in ge] for _, ge in recs]
+    K = args.steps
+    dec_avg = sum(dec_ms) / K
+    exact_avg = sum(exact_ms) / K
+    mfma_avg = sum(mfma_ms) / K
+    value = decode_bytes / (dec_avg * 1e-3) / 1e9
+
+    # the GEMV kernel (vec_dot_v8): average launch duration over every launch
+    n_gemv = len(gemv_launches)
+    gemv_avg_ms = sum(sum(r) for r in gemv_ms) / (K * n_gemv)
+    gemv_avg_bytes = sum(gemv_b) / n_gemv
+    achieved = gemv_avg_bytes / (gemv_avg_ms * 1e-3) / 1e9
+    per_launch = {name: {"bytes": gemv_b[i], "avg_us": round(1e3 * sum(r[i] for r in gemv_ms) / K, 2),
+                         "GB_s": round(gemv_b[i] / (sum(r[i] for r in gemv_ms) / K * 1e-3) / 1e9, 1)}
+                  for i, (name, _, _) in enumerate(gemv_launches)}
+
+    rec = traffic_record(os.path.join(ROOT, "f16_weight_matrix_amd", "csrc", "vec_dot.hip"))
+    traffic = None
+    if rec is not None:
+        traffic = rec.get("bytes_per_launch")
+
+    exact_tflops = flops_n512 / (exact_avg * 1e-3) / 1e12
+    mfma_tflops = flops_n512 / (mfma_avg * 1e-3) / 1e12
+
+    out = {
+        "metric": "F16 GEMV GB/s (n=1) and GEMM TFLOP/s (n=512), % of MI355X roofline",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * wall_s / K, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 inputs, f32 FMA accumulation (exact ggml orders); fp16 MFMA for the fast path",
+        "data": "synthetic: seeded N(0,0.02) f16 weights, N(0,1) f32 activations",
+        "config": {
+            "workload": "Llama-3-8B-shaped F16 set (q/o 4096x4096, k/v 1024x4096, gate/up 14336x4096, "
+                        "down 4096x14336, logits 128256x4096): decode GEMV n=1 + prefill n=512 exact and MFMA",
+            "decode_bytes_per_step": decode_bytes,
+            "prefill_flops_per_product_set": flops_n512,
+            "parallelism": "single GPU",
+        },
+        "phases_ms": {"decode": round(dec_avg, 4), "prefill_exact": round(exact_avg, 4),
+                      "prefill_mfma": round(mfma_avg, 4)},
+        "roofline": {
+            "kernel": "vec_dot_v8 (GEMV, vec_dot order)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(gemv_avg_ms * 1e3, 2),
+            "avg_launch_bytes": gemv_avg_bytes,
+            "per_launch": per_launch,
+        },
+        "gemm_n512": {
+            "exact": {"kernel": "sgemm_kernel (tinyBLAS order)", "bound": "alu",
+                      "achieved": round(exact_tflops, 2), "unit": "TFLOP/s",
+                      "peak": VALU_FP32_PEAK_TFLOPS, "frac": round(exact_tflops / VALU_FP32_PEAK_TFLOPS, 4),
+                      "frac_of_nonpacked_fma_peak": round(exact_tflops / VALU_FP32_NONPACKED_TFLOPS, 4)},
+            "mfma": {"kernel": "mfma_kernel (fp16 MFMA)", "bound": "mfma",
+                     "achieved": round(mfma_tflops, 1), "unit": "TFLOP/s",
+                     "peak": MFMA_F16_PEAK_TFLOPS, "frac": round(mfma_tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+        },
+        "setup_s": round(setup_s, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(host_w, dec, dec_k, S, N, args.cpu_sample_rows, value)
+
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(host_w, dec, dec_k, S, N, sample_div, gpu_value):
+    """The oracle as it stands, on the host cores: the full decode GEMV set
+    (same inputs), and the exact n = 512 products on the first rows/N rows of
+    every matrix."""
+    import numpy as np
+
+    import oracle
+
+    orc = oracle.default()
+    T = cpu_threads()
+    src = {"q": "attn", "k": "attn", "v": "attn", "o": "o", "gate": "ffn", "up": "ffn", "down": "down",
+           "logits": "logits"}
+    a16 = {g: orc.to_f16(dec[i, :dec_k[g]]) for i, g in enumerate(dec_k)}
+    t = time.perf_counter()
+    nbytes = 0
+    for m, w in host_w.items():
+        k = dec_k[src[m]]
+        orc.mat_vec(w, a16[src[m]], threads=T)
+        nbytes += 2 * w.shape[0] * k + 2 * k + 4 * w.shape[0]
+    dt_gemv = time.perf_counter() - t
+    import synth
+    pre = synth.activation(synth.CFG_8B_PREFILL, 0, 0, N, 14336)
+    flops = 0
+    t = time.perf_counter()
+    for m, w in host_w.items():
+        k = dec_k[src[m]]
+        rows = max(4, (w.shape[0] // sample_div) // 4 * 4)
+        orc.mat_mul(w[:rows], orc.to_f16(pre[:, :k]), threads=T)
+        flops += 2 * rows * k * N
+    dt_mm = time.perf_counter() - t
+    return {
+        "value": round(nbytes / dt_gemv / 1e9, 3),
+        "unit": "GB/s",
+        "cores": T,
+        "kind": "oracle",
+        "sample": "decode: the full 8B GEMV set (%d bytes, %.2f s); prefill exact: the first 1/%d of the rows "
+                  "of every matrix at n=512 (%.3g FLOP, %.2f s)" % (nbytes, dt_gemv, sample_div, flops, dt_mm),
+        "gemm_exact_tflops": round(flops / dt_mm / 1e12, 5),
+        "gpu_over_cpu": round(gpu_value / (nbytes / dt_gemv / 1e9), 1),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+"""f16wm: F16-weight matrix products for AMD MI355X (gfx950).
+
+A thin binding over the C ABI in ``include/f16wm.h`` (``libf16wm.so``, built
+by ``python -m f16_weight_matrix_amd.build``).  Every step of every product runs
+in the library's HIP kernels; this module only checks tensors and passes their
+device pointers and the current HIP stream.  PyTorch supplies device memory
+and streams, nothing else.  There is no CPU fallback: if the library is not
+built, importing the functions raises.
+
+Tensors: f16 data (weights ``[rows, k]``, rounded activations ``[n, k]``) is
+``torch.float16`` (or ``int16``/``uint16`` holding the same bit patterns),
+contiguous, on a gfx950 device; f32 data is ``torch.float32``.  Outputs of
+products are ``[n, rows]`` (``out[c*rows + r]``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libf16wm.so")
+
+F16WM_OK = 0
+F16WM_EINVAL = -1
+F16WM_ENODEV = -2
+F16WM_ELAUNCH = -3
+F16WM_EUNSUPPORTED = -4
+MAX_MULTI = 8
+
+
+class F16WMError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s (code %d)" % (msg, code))
+        self.code = code
+
+
+class _Mat(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("rows", ctypes.c_int64), ("out", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libf16wm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libf16wm.so is not built (%s); run `python -m f16_weight_matrix_amd.build`"
+                               % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.f16wm_to_f16.argtypes = [P, P, I64, P]
+        L.f16wm_mat_vec.argtypes = [P, I64, I64, P, P, P]
+        L.f16wm_mat_vec_multi.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, P]
+        L.f16wm_mat_mul.argtypes = [P, I64, I64, P, I64, P, P]
+        L.f16wm_mat_mul_mfma.argtypes = [P, I64, I64, P, I64, P, P]
+        L.f16wm_takes_sgemm.argtypes = [I64, I64, I64]
+        for f in ("f16wm_to_f16", "f16wm_mat_vec", "f16wm_mat_vec_multi", "f16wm_mat_mul",
+                  "f16wm_mat_mul_mfma", "f16wm_takes_sgemm"):
+            getattr(L, f).restype = ctypes.c_int
+        L.f16wm_last_error.restype = ctypes.c_char_p
+        L.f16wm_last_error.argtypes = []
+        L.f16wm_version.restype = ctypes.c_char_p
+        L.f16wm_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().f16wm_last_error().decode()
+
+
+def version() -> str:
+    return lib().f16wm_version().decode()
+
+
+def takes_sgemm(rows: int, k: int, n: int) -> bool:
+    """n >= 2 and rows % 4 == 0 and k % 8 == 0: the tinyBLAS order applies."""
+    return bool(lib().f16wm_takes_sgemm(rows, k, n))
+
+
+_F16_DTYPES = (torch.float16, torch.int16, torch.uint16)
+
+
+def _f16(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.dtype not in _F16_DTYPES:
+        raise TypeError("%s must hold f16 bit patterns (float16/int16/uint16), got %s" % (name, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be on a GPU" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _f32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.float32:
+        raise TypeError("%s must be float32, got %s" % (name, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be on a GPU" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _check(rc: int):
+    if rc != F16WM_OK:
+        raise F16WMError(rc, last_error())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def to_f16(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Round f32 activations to f16 (nearest even): the same shape in float16."""
+    _f32(x, "x")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float16, device=x.device)
+    _f16(out, "out")
+    if out.numel() != x.numel() or out.device != x.device:
+        raise ValueError("out must match x in size and device")
+    with torch.cuda.device(x.device):
+        _check(lib().f16wm_to_f16(x.data_ptr(), out.data_ptr(), x.numel(), _stream(x.device)))
+    return out
+
+
+def _wk(w: torch.Tensor):
+    _f16(w, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be [rows, k]")
+    return w.shape[0], w.shape[1]
+
+
+def mat_vec(w: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """out[r] = vec_dot(W[r], a): W [rows, k] f16, a [k] f16 -> [rows] f32."""
+    rows, k = _wk(w)
+    _f16(a, "a")
+    if a.numel() != k:
+        raise ValueError("a must have k = %d elements" % k)
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=w.device)
+    _f32(out, "out")
+    if out.numel() != rows:
+        raise ValueError("out must have rows = %d elements" % rows)
+    with torch.cuda.device(w.device):
+        _check(lib().f16wm_mat_vec(w.data_ptr(), rows, k, a.data_ptr(), out.data_ptr(), _stream(w.device)))
+    return out
+
+
+def mat_vec_multi(ws, a: torch.Tensor, outs=None) -> list:
+    """Several matrices with the same k times one f16 column, in one launch."""
+    ws = list(ws)
+    if not 1 <= len(ws) <= MAX_MULTI:
+        raise ValueError("1..%d matrices" % MAX_MULTI)
+    k = None
+    for w in ws:
+        rows, kk = _wk(w)
+        if k is None:
+            k = kk
+        elif kk != k:
+            raise ValueError("all matrices must share k")
+    _f16(a, "a")
+    if a.numel() != k:
+        raise ValueError("a must have k = %d elements" % k)
+    if outs is None:
+        outs = [torch.empty(w.shape[0], dtype=torch.float32, device=w.device) for w in ws]
+    outs = list(outs)
+    if len(outs) != len(ws):
+        raise ValueError("one output per matrix")
+    mats = (_Mat * len(ws))()
+    for i, (w, o) in enumerate(zip(ws, outs)):
+        _f32(o, "outs[%d]" % i)
+        if o.numel() != w.shape[0]:
+            raise ValueError("outs[%d] must have %d elements" % (i, w.shape[0]))
+        mats[i].w = w.data_ptr()
+        mats[i].rows = w.shape[0]
+        mats[i].out = o.data_ptr()
+    dev = ws[0].device
+    with torch.cuda.device(dev):
+        _check(lib().f16wm_mat_vec_multi(mats, len(ws), k, a.data_ptr(), _stream(dev)))
+    return outs
+
+
+def _mm(fn, w, a, out):
+    rows, k = _wk(w)
+    _f16(a, "a")
+    if a.dim() == 1:
+        a = a.view(1, -1)
+    if a.dim() != 2 or a.shape[1] != k:
+        raise ValueError("a must be [n, k] with k = %d" % k)
+    n = a.shape[0]
+    if out is None:
+        out = torch.empty((n, rows), dtype=torch.float32, device=w.device)
+    _f32(out, "out")
+    if out.numel() != n * rows:
+        raise ValueError("out must have n*rows = %d elements" % (n * rows))
+    with torch.cuda.device(w.device):
+        _check(fn(w.data_ptr(), rows, k, a.data_ptr(), n, out.data_ptr(), _stream(w.device)))
+    return out
+
+
+def mat_mul(w: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Exact product in ggml's order for the shape: W [rows, k] x A [n, k] -> [n, rows] f32."""
+    return _mm(lib().f16wm_mat_mul, w, a, out)
+
+
+def mat_mul_mfma(w: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The same product on the fp16 matrix cores (approximate, f32 accumulation)."""
+    return _mm(lib().f16wm_mat_mul_mfma, w, a, out)

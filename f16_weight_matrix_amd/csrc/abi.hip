@@ -1,0 +1,232 @@
+// The f16wm C ABI: host-side validation, the shape-based choice of float
+// order, and the kernel launches.  No entry point allocates memory or
+// synchronises; every launch goes to the caller's stream.
+//
+// Path choice: bankML f16 page, Technical usage and Design notes.  One column
+// (and every shape for which takes_sgemm is false) uses the vec_dot order;
+// n >= 2 with rows % 4 == 0 and k % 8 == 0 uses the tinyBLAS order.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok()
+{
+    g_err.clear();
+    return F16WM_OK;
+}
+
+// Largest element count accepted for one array (keeps every byte offset and
+// grid computation far inside int64 / uint32 ranges).
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+bool mul_ok(int64_t a, int64_t b, int64_t *r)
+{
+    if (a < 0 || b < 0) return false;
+    if (__builtin_mul_overflow(a, b, r)) return false;
+    return *r <= kMaxElems;
+}
+
+struct Span {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+Span span(const void *p, int64_t bytes) { return {(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes}; }
+bool overlap(Span x, Span y) { return x.lo < y.hi && y.lo < x.hi && x.lo != x.hi && y.lo != y.hi; }
+
+// Device admission: the current device must be a gfx950.  Cached per device.
+std::atomic<int> g_dev_state[64];   // 0 unknown, 1 ok, 2 refused
+
+int check_device(const char *fn)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0)
+        return fail(F16WM_ENODEV, "%s: no HIP device is current (%s)", fn,
+                    e != hipSuccess ? hipGetErrorString(e) : "none");
+    if (dev < 64) {
+        int st = g_dev_state[dev].load(std::memory_order_relaxed);
+        if (st == 1) return F16WM_OK;
+        if (st == 2) return fail(F16WM_ENODEV, "%s: device %d is not a gfx950", fn, dev);
+    }
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+        return fail(F16WM_ENODEV, "%s: hipGetDeviceProperties(%d) failed: %s", fn, dev,
+                    hipGetErrorString(e));
+    const bool good = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_dev_state[dev].store(good ? 1 : 2, std::memory_order_relaxed);
+    if (!good)
+        return fail(F16WM_ENODEV, "%s: device %d is %s, this library is built for gfx950", fn, dev,
+                    prop.gcnArchName);
+    return F16WM_OK;
+}
+
+int launched(const char *fn, hipError_t e)
+{
+    if (e != hipSuccess) return fail(F16WM_ELAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned(const void *p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+// Checks common to the products: sizes, overflow, null pointers, alignment.
+int check_product(const char *fn, const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a,
+                  int64_t n, const float *out, int64_t *w_elems, int64_t *a_elems, int64_t *o_elems)
+{
+    if (rows < 0 || k < 0 || n < 0)
+        return fail(F16WM_EINVAL, "%s: negative size (rows=%lld k=%lld n=%lld)", fn, (long long)rows,
+                    (long long)k, (long long)n);
+    if (!mul_ok(rows, k, w_elems) || !mul_ok(n, k, a_elems) || !mul_ok(n, rows, o_elems))
+        return fail(F16WM_EINVAL, "%s: size too large (rows=%lld k=%lld n=%lld; limit 2^40 elements)",
+                    fn, (long long)rows, (long long)k, (long long)n);
+    if ((*w_elems > 0 && !w) || (*a_elems > 0 && !a) || (*o_elems > 0 && !out))
+        return fail(F16WM_EINVAL, "%s: null pointer for a non-empty array", fn);
+    if (!aligned(w, 2) || !aligned(a, 2) || !aligned(out, 4))
+        return fail(F16WM_EINVAL, "%s: misaligned pointer (f16 arrays need 2 bytes, f32 arrays 4)", fn);
+    const Span so = span(out, *o_elems * 4);
+    if (overlap(so, span(w, *w_elems * 2)) || overlap(so, span(a, *a_elems * 2)))
+        return fail(F16WM_EINVAL, "%s: output overlaps an input", fn);
+    return F16WM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *f16wm_last_error(void) { return g_err.c_str(); }
+
+const char *f16wm_version(void) { return "f16wm 0.1 (gfx950)"; }
+
+int f16wm_takes_sgemm(int64_t rows, int64_t k, int64_t n)
+{
+    if (rows < 0 || k < 0 || n < 0) return 0;
+    return (n >= 2 && rows % 4 == 0 && k % 8 == 0) ? 1 : 0;
+}
+
+int f16wm_to_f16(const float *x, uint16_t *y, int64_t count, void *stream)
+{
+    const char *fn = "f16wm_to_f16";
+    if (count < 0 || count > kMaxElems)
+        return fail(F16WM_EINVAL, "%s: bad count %lld", fn, (long long)count);
+    if (count == 0) return ok();
+    if (!x || !y) return fail(F16WM_EINVAL, "%s: null pointer", fn);
+    if (!aligned(x, 4) || !aligned(y, 2)) return fail(F16WM_EINVAL, "%s: misaligned pointer", fn);
+    if (overlap(span(x, count * 4), span(y, count * 2)))
+        return fail(F16WM_EINVAL, "%s: output overlaps the input", fn);
+    if (int rc = check_device(fn)) return rc;
+    return launched(fn, f16wm::launch_to_f16(x, y, count, (hipStream_t)stream));
+}
+
+int f16wm_mat_vec(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, float *out,
+                  void *stream)
+{
+    const char *fn = "f16wm_mat_vec";
+    int64_t we, ae, oe;
+    if (int rc = check_product(fn, w, rows, k, a, 1, out, &we, &ae, &oe)) return rc;
+    if (rows == 0) return ok();
+    if (int rc = check_device(fn)) return rc;
+    f16wm::RowTable t = {};
+    t.count = 1;
+    t.w[0] = w;
+    t.out[0] = out;
+    t.row0[0] = 0;
+    t.row0[1] = rows;
+    const bool vec8 = k % 8 == 0 && aligned(w, 16) && aligned(a, 16);
+    return launched(fn, f16wm::launch_vec_dot(t, k, a, 1, vec8, (hipStream_t)stream));
+}
+
+int f16wm_mat_vec_multi(const f16wm_mat *mats, int32_t count, int64_t k, const uint16_t *a,
+                        void *stream)
+{
+    const char *fn = "f16wm_mat_vec_multi";
+    if (count < 1 || count > F16WM_MAX_MULTI)
+        return fail(F16WM_EINVAL, "%s: count %d outside 1..%d", fn, (int)count, F16WM_MAX_MULTI);
+    if (!mats) return fail(F16WM_EINVAL, "%s: null descriptor array", fn);
+    f16wm::RowTable t = {};
+    t.count = count;
+    bool vec8 = k % 8 == 0 && aligned(a, 16);
+    int64_t total = 0;
+    for (int m = 0; m < count; m++) {
+        int64_t we, ae, oe;
+        char name[64];
+        snprintf(name, sizeof name, "%s[%d]", fn, m);
+        if (int rc = check_product(name, mats[m].w, mats[m].rows, k, a, 1, mats[m].out, &we, &ae, &oe))
+            return rc;
+        for (int j = 0; j < m; j++) {
+            // no output may overlap another matrix or another output
+            const Span sm = span(mats[m].out, mats[m].rows * 4);
+            if (overlap(sm, span(mats[j].out, mats[j].rows * 4)) ||
+                overlap(sm, span(mats[j].w, mats[j].rows * k * 2)) ||
+                overlap(span(mats[j].out, mats[j].rows * 4), span(mats[m].w, mats[m].rows * k * 2)))
+                return fail(F16WM_EINVAL, "%s: outputs of matrices %d and %d overlap another array", fn,
+                            j, m);
+        }
+        t.w[m] = mats[m].w;
+        t.out[m] = mats[m].out;
+        t.row0[m] = total;
+        total += mats[m].rows;
+        if (total > kMaxElems) return fail(F16WM_EINVAL, "%s: too many rows", fn);
+        vec8 = vec8 && aligned(mats[m].w, 16);
+    }
+    t.row0[count] = total;
+    if (total == 0) return ok();
+    if (int rc = check_device(fn)) return rc;
+    return launched(fn, f16wm::launch_vec_dot(t, k, a, 1, vec8, (hipStream_t)stream));
+}
+
+int f16wm_mat_mul(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
+                  float *out, void *stream)
+{
+    const char *fn = "f16wm_mat_mul";
+    int64_t we, ae, oe;
+    if (int rc = check_product(fn, w, rows, k, a, n, out, &we, &ae, &oe)) return rc;
+    if (rows == 0 || n == 0) return ok();
+    if (int rc = check_device(fn)) return rc;
+    const bool al16 = aligned(w, 16) && aligned(a, 16);
+    if (f16wm_takes_sgemm(rows, k, n))
+        return launched(fn, f16wm::launch_sgemm(w, rows, k, a, n, out, al16, (hipStream_t)stream));
+    f16wm::RowTable t = {};
+    t.count = 1;
+    t.w[0] = w;
+    t.out[0] = out;
+    t.row0[0] = 0;
+    t.row0[1] = rows;
+    const bool vec8 = k % 8 == 0 && al16;
+    return launched(fn, f16wm::launch_vec_dot(t, k, a, n, vec8, (hipStream_t)stream));
+}
+
+int f16wm_mat_mul_mfma(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
+                       float *out, void *stream)
+{
+    const char *fn = "f16wm_mat_mul_mfma";
+    int64_t we, ae, oe;
+    if (int rc = check_product(fn, w, rows, k, a, n, out, &we, &ae, &oe)) return rc;
+    if (k % 8 != 0 || !aligned(w, 16) || !aligned(a, 16))
+        return fail(F16WM_EUNSUPPORTED, "%s: needs k %% 8 == 0 and 16-byte aligned w and a (k=%lld)", fn,
+                    (long long)k);
+    if (rows == 0 || n == 0) return ok();
+    if (int rc = check_device(fn)) return rc;
+    return launched(fn, f16wm::launch_mfma(w, rows, k, a, n, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Internal declarations shared by the f16wm HIP sources (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "f16wm.h"
+
+namespace f16wm {
+
+// Rows of up to F16WM_MAX_MULTI matrices that share k and one activation,
+// laid end to end: global row g belongs to matrix m when
+// row0[m] <= g < row0[m + 1].
+struct RowTable {
+    const uint16_t *w[F16WM_MAX_MULTI];
+    float *out[F16WM_MAX_MULTI];
+    int64_t row0[F16WM_MAX_MULTI + 1];
+    int32_t count;
+};
+
+// Every launcher enqueues on `stream` and returns the hipError_t of the launch.
+hipError_t launch_to_f16(const float *x, uint16_t *y, int64_t count, hipStream_t stream);
+
+// vec_dot order for `ncols` activation columns (column c at a + c*k, output
+// of matrix m column c at out[m] + c*rows_m).  vec8 needs k % 8 == 0 and
+// 16-byte aligned w[] and a.
+hipError_t launch_vec_dot(const RowTable &t, int64_t k, const uint16_t *a, int64_t ncols,
+                          bool vec8, hipStream_t stream);
+
+// tinyBLAS order (rows % 4 == 0, k % 8 == 0, n >= 2 checked by the caller).
+// aligned16: w and a are 16-byte aligned.
+hipError_t launch_sgemm(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
+                        float *out, bool aligned16, hipStream_t stream);
+
+// fp16 MFMA product (k % 8 == 0, w and a 16-byte aligned).
+hipError_t launch_mfma(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
+                       float *out, hipStream_t stream);
+
+}  // namespace f16wm

@@ -1,0 +1,126 @@
+/*
+ * f16wm -- F16-weight matrix products on AMD MI355X (gfx950), C ABI.
+ *
+ * The operations are those of the bankML documentation page "bankML/f16.rs --
+ * F16 weights, multiplied as the shipped ggml b11192 multiplies them" (cited
+ * as "f16 page" with its section names).  An F16 weight matrix W is rows x k
+ * IEEE binary16 values, row-major, k contiguous (little-endian, as the page
+ * requires).  Activations are f32 columns rounded to f16 by f16wm_to_f16 and
+ * then shared by every product that reads them (bankML page "bankML/forward.rs",
+ * Advantages and efficiency: one rounded activation feeds Q, K and V, another
+ * feeds gate and up).
+ *
+ * Conventions for every entry point below:
+ *  - All array pointers are DEVICE pointers owned by the caller.  The library
+ *    reads/writes them in stream order during the call's kernels and keeps no
+ *    reference afterwards; it never frees them and allocates no memory.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls are
+ *    asynchronous: they enqueue kernels and return without synchronising.
+ *  - Validation happens on the host before any launch.  On failure nothing is
+ *    launched, a negative F16WM_E* code is returned and f16wm_last_error()
+ *    gives the reason (per calling thread).
+ *  - Sizes are element counts (int64_t).  Zero-sized products are no-ops that
+ *    return F16WM_OK.  Outputs may not overlap inputs (F16WM_EINVAL).
+ *  - Every f16 pointer must be 2-byte aligned and every f32 pointer 4-byte
+ *    aligned.  Greater alignment (16 bytes, with k % 8 == 0) selects the
+ *    vectorised kernels; the bits are the same either way.
+ */
+#ifndef F16WM_H
+#define F16WM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define F16WM_OK 0
+#define F16WM_EINVAL (-1)      /* bad argument: null, negative, overflow, alignment, overlap */
+#define F16WM_ENODEV (-2)      /* no usable gfx950 device is current */
+#define F16WM_ELAUNCH (-3)     /* the HIP runtime refused a launch */
+#define F16WM_EUNSUPPORTED (-4) /* a valid shape this entry point does not take */
+
+#define F16WM_MAX_MULTI 8      /* matrices per f16wm_mat_vec_multi call */
+
+/* One matrix of a grouped product: W (rows x k, f16) and its output (rows f32). */
+typedef struct {
+    const uint16_t *w;
+    int64_t rows;
+    float *out;
+} f16wm_mat;
+
+/*
+ * f16wm_to_f16: y[i] = f16(x[i]), binary32 -> binary16, round to nearest,
+ * ties to even; overflow gives +-inf, results below 2^-14 become f16
+ * subnormals, NaN gives a quiet NaN with the sign and top ten payload bits.
+ * f16 page, Design notes ("Activation"): the activation is rounded this way
+ * before every product.  x: count f32, y: count f16 (bit patterns).
+ */
+int f16wm_to_f16(const float *x, uint16_t *y, int64_t count, void *stream);
+
+/*
+ * f16wm_mat_vec: out[r] = vec_dot(W[r], a) for r < rows.
+ * f16 page, Matrix products (mat_vec_par) and Design notes ("vec_dot"): each
+ * row is four 8-lane f32 FMA accumulators over 32-element steps (accumulator
+ * j lane l takes elements 32t + 8j + l), reduced (a0+a2)+(a1+a3), then low four
+ * lanes + high four, then two horizontal adds of adjacent pairs; the k % 32
+ * tail is added to that f32 in binary64, ascending, and the sum is rounded to
+ * f32.  w: rows x k f16, a: k f16, out: rows f32.  k = 0 writes +0.0.
+ */
+int f16wm_mat_vec(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, float *out,
+                  void *stream);
+
+/*
+ * f16wm_mat_vec_multi: for each of `count` matrices (1..F16WM_MAX_MULTI, all
+ * with the same k) mats[m].out[r] = vec_dot(mats[m].w[r], a), in ONE launch.
+ * f16 page, Matrix products (mat_vec_multi_par): Q, K and V, or gate and up,
+ * by one column in one pass; every row is still one vec_dot.  `mats` is a
+ * HOST array of `count` descriptors (read during the call only); the
+ * pointers inside are device pointers.  Outputs may not overlap each other.
+ */
+int f16wm_mat_vec_multi(const f16wm_mat *mats, int32_t count, int64_t k, const uint16_t *a,
+                        void *stream);
+
+/*
+ * f16wm_mat_mul: out[c*rows + r] = dot(W[r], A[c]) for r < rows, c < n, with
+ * the float order ggml picks by shape (f16 page, Matrix products mat_mul_par
+ * and Design notes "sgemm_dot"): when f16wm_takes_sgemm(rows, k, n), every
+ * element is one 8-lane FMA chain (lane l takes elements 8t + l, ascending t)
+ * reduced ((l0+l4)+(l2+l6))+((l1+l5)+(l3+l7)); otherwise every element is
+ * vec_dot as in f16wm_mat_vec.  Bit-exact: the kernel tiling never changes an
+ * element's order.  w: rows x k f16; a: n x k f16 (column c at a + c*k);
+ * out: n x rows f32.  n = 1 equals f16wm_mat_vec.
+ */
+int f16wm_mat_mul(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
+                  float *out, void *stream);
+
+/*
+ * f16wm_mat_mul_mfma: the same product and layout as f16wm_mat_mul computed on
+ * the fp16 matrix cores (MFMA, f16 x f16 products, f32 accumulation).  An
+ * approximate fast path for prefill micro-batches (bankML page
+ * "bankML/forward.rs", Technical usage: prompts run in micro-batches of up to
+ * 512 columns): its summation order is the hardware's, so it is NOT bit-equal
+ * to either ggml order; its error against a binary64 sum is bounded instead.
+ * Requires k % 8 == 0 and 16-byte aligned w and a (F16WM_EUNSUPPORTED else).
+ */
+int f16wm_mat_mul_mfma(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
+                       float *out, void *stream);
+
+/*
+ * f16wm_takes_sgemm: 1 when n >= 2 && rows % 4 == 0 && k % 8 == 0, else 0
+ * (f16 page, Technical usage).  Pure host function, no device needed.
+ * Negative arguments give 0.
+ */
+int f16wm_takes_sgemm(int64_t rows, int64_t k, int64_t n);
+
+/* The reason for the calling thread's last failed call ("" if none). */
+const char *f16wm_last_error(void);
+
+/* Library version string. */
+const char *f16wm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* F16WM_H */

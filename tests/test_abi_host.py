@@ -1,0 +1,152 @@
+"""Host-side checks of the C-ABI library: it loads, exports every function the
+header declares, and rejects bad arguments before any launch.  No kernel is
+launched here; the GPU tests cover the compute.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import f16_weight_matrix_amd as f16wm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "f16wm.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(f16wm_[a-z0-9_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return f16wm.lib()
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted([
+        "f16wm_to_f16", "f16wm_mat_vec", "f16wm_mat_vec_multi", "f16wm_mat_mul",
+        "f16wm_mat_mul_mfma", "f16wm_takes_sgemm", "f16wm_last_error", "f16wm_version"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_exports_are_c_symbols():
+    """extern "C": the dynamic symbol table holds the plain names."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", f16wm.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    names = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared():
+        assert name in names, name
+
+
+def test_version(L):
+    assert "gfx950" in f16wm.version()
+
+
+def test_takes_sgemm_rule(L):
+    """The library's rule equals the page's n >= 2 && rows % 4 == 0 && k % 8 == 0
+    over a grid of shapes; negative sizes give 0."""
+    for rows in range(0, 20):
+        for k in range(0, 40):
+            for n in range(0, 5):
+                want = n >= 2 and rows % 4 == 0 and k % 8 == 0
+                assert f16wm.takes_sgemm(rows, k, n) is want, (rows, k, n)
+    assert not f16wm.takes_sgemm(-4, 8, 2)
+    assert not f16wm.takes_sgemm(4, -8, 2)
+    assert not f16wm.takes_sgemm(4, 8, -2)
+
+
+# Fake, never dereferenced device addresses: validation rejects before launch.
+P = 1 << 40
+STREAM = None
+
+
+def _err(rc):
+    assert rc == f16wm.F16WM_EINVAL, (rc, f16wm.last_error())
+    return f16wm.last_error()
+
+
+def test_mat_vec_rejects_bad_arguments(L):
+    assert "negative" in _err(L.f16wm_mat_vec(P, -1, 8, P + 4096, P + 8192, STREAM))
+    assert "negative" in _err(L.f16wm_mat_vec(P, 4, -8, P + 4096, P + 8192, STREAM))
+    assert "null" in _err(L.f16wm_mat_vec(None, 4, 8, P + 4096, P + 8192, STREAM))
+    assert "null" in _err(L.f16wm_mat_vec(P, 4, 8, None, P + 8192, STREAM))
+    assert "null" in _err(L.f16wm_mat_vec(P, 4, 8, P + 4096, None, STREAM))
+    assert "misaligned" in _err(L.f16wm_mat_vec(P + 1, 4, 8, P + 4096, P + 8192, STREAM))
+    assert "misaligned" in _err(L.f16wm_mat_vec(P, 4, 8, P + 4096, P + 8194, STREAM))
+    assert "too large" in _err(L.f16wm_mat_vec(P, 1 << 31, 1 << 31, P + 4096, P + 8192, STREAM))
+    # out (4 rows x 4 bytes) overlapping w (4 x 8 x 2 bytes)
+    assert "overlap" in _err(L.f16wm_mat_vec(P, 4, 8, P + 4096, P + 16, STREAM))
+    assert "overlap" in _err(L.f16wm_mat_vec(P, 4, 8, P + 4096, P + 4096, STREAM))
+
+
+def test_mat_mul_rejects_bad_arguments(L):
+    assert "negative" in _err(L.f16wm_mat_mul(P, 4, 8, P + 4096, -1, P + 8192, STREAM))
+    assert "overlap" in _err(L.f16wm_mat_mul(P, 4, 8, P + 4096, 3, P + 4100, STREAM))
+    assert "null" in _err(L.f16wm_mat_mul(P, 4, 8, None, 3, P + 8192, STREAM))
+    assert "too large" in _err(L.f16wm_mat_mul(P, 1 << 21, 8, P, 1 << 21, P, STREAM))
+
+
+def test_mat_mul_mfma_rejects_unsupported(L):
+    rc = L.f16wm_mat_mul_mfma(P, 4, 12, P + 4096, 3, P + 8192, STREAM)
+    assert rc == f16wm.F16WM_EUNSUPPORTED and "k % 8" in f16wm.last_error()
+    rc = L.f16wm_mat_mul_mfma(P + 2, 4, 16, P + 4096, 3, P + 8192, STREAM)
+    assert rc == f16wm.F16WM_EUNSUPPORTED
+
+
+def test_to_f16_rejects_bad_arguments(L):
+    assert "bad count" in _err(L.f16wm_to_f16(P, P + 4096, -1, STREAM))
+    assert "null" in _err(L.f16wm_to_f16(None, P + 4096, 4, STREAM))
+    assert "misaligned" in _err(L.f16wm_to_f16(P + 2, P + 4096, 4, STREAM))
+    assert "overlap" in _err(L.f16wm_to_f16(P, P + 8, 4, STREAM))
+
+
+def test_mat_vec_multi_rejects_bad_arguments(L):
+    Mat = f16wm._Mat
+    mats = (Mat * 2)()
+    mats[0].w, mats[0].rows, mats[0].out = P, 4, P + (1 << 20)
+    mats[1].w, mats[1].rows, mats[1].out = P + 4096, 4, P + (1 << 20) + 8   # overlaps out[0]
+    assert "overlap" in _err(L.f16wm_mat_vec_multi(mats, 2, 8, P + (1 << 21), STREAM))
+    assert "count" in _err(L.f16wm_mat_vec_multi(mats, 0, 8, P + (1 << 21), STREAM))
+    assert "count" in _err(L.f16wm_mat_vec_multi(mats, 9, 8, P + (1 << 21), STREAM))
+    assert "null" in _err(L.f16wm_mat_vec_multi(None, 2, 8, P + (1 << 21), STREAM))
+    mats[1].out = P + (1 << 20) + 4096
+    mats[1].rows = -1
+    assert "negative" in _err(L.f16wm_mat_vec_multi(mats, 2, 8, P + (1 << 21), STREAM))
+
+
+def test_empty_products_are_no_ops(L):
+    """rows = 0 or n = 0: nothing to do, success without touching a device."""
+    assert L.f16wm_mat_vec(P, 0, 8, P + 4096, P + 8192, STREAM) == 0
+    assert L.f16wm_mat_mul(P, 4, 8, P + 4096, 0, P + 8192, STREAM) == 0
+    assert L.f16wm_mat_mul(P, 0, 8, P + 4096, 3, P + 8192, STREAM) == 0
+    assert L.f16wm_mat_mul_mfma(P, 0, 8, P + 4096, 3, P + 8192, STREAM) == 0
+    assert L.f16wm_to_f16(P, P + 4096, 0, STREAM) == 0
+    assert f16wm.last_error() == ""
+
+
+def test_no_device_is_reported_not_launched(L):
+    """Valid arguments with no GPU present: F16WM_ENODEV, nothing launched."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc = L.f16wm_mat_vec(P, 4, 8, P + 4096, P + 8192, STREAM)
+    assert rc == f16wm.F16WM_ENODEV, (rc, f16wm.last_error())
+    assert "device" in f16wm.last_error()
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    w = torch.zeros(4, 8, dtype=torch.float16)
+    a = torch.zeros(8, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        f16wm.mat_vec(w, a)
+    with pytest.raises(TypeError):
+        f16wm.mat_vec(w.float(), a)

@@ -1,0 +1,423 @@
+"""GPU parity: the HIP library through its C ABI against the oracle, element by
+element, on the same seeded inputs.
+
+Exact paths (to_f16, vec_dot, tinyBLAS) must be bit-identical to the oracle
+(NaN compared as "is NaN").  The MFMA fast path must stay within
+max |y - ref| / sum_i |w_i a_i| <= 2e-3 of the binary64 reference.
+Full-size products are checked completely where the oracle is fast enough
+(every n = 1 product, layer 0 of the 135M prefill) and on sampled elements
+otherwise (the oracle computes each sampled element with the full shape's
+order).
+"""
+import concurrent.futures as cf
+import os
+
+import numpy as np
+import pytest
+
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import f16_weight_matrix_amd as f16wm  # noqa: E402
+
+DEV = torch.device("cuda:0")
+MFMA_TOL = 2e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def up16(x: np.ndarray, offset: int = 0) -> torch.Tensor:
+    """uint16 numpy -> float16 GPU tensor (optionally at an element offset
+    inside a larger allocation, to test misaligned pointers)."""
+    flat = torch.from_numpy(np.ascontiguousarray(x).view(np.int16).reshape(-1)).to(DEV)
+    if offset:
+        buf = torch.empty(flat.numel() + offset, dtype=torch.int16, device=DEV)
+        buf[offset:] = flat
+        flat = buf[offset:]
+    return flat.view(torch.float16).view(x.shape)
+
+
+def up32(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().view(np.uint32)
+
+
+def assert_bits_equal(got: np.ndarray, want: np.ndarray, what: str):
+    got = np.ascontiguousarray(got, dtype=np.float32)
+    want = np.ascontiguousarray(want, dtype=np.float32)
+    assert got.shape == want.shape, what
+    gn, wn = np.isnan(got), np.isnan(want)
+    same = (got.view(np.uint32) == want.view(np.uint32)) | (gn & wn)
+    if not same.all():
+        idx = np.argwhere(~same)
+        i = tuple(idx[0])
+        raise AssertionError("%s: %d of %d elements differ; first at %s: got %r (0x%08x) want %r (0x%08x)"
+                             % (what, len(idx), got.size, i, float(got[i]), got.view(np.uint32)[i],
+                                float(want[i]), want.view(np.uint32)[i]))
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    return oracle.default()
+
+
+# ------------------------------------------------------------------ to_f16
+
+def test_to_f16_matches_oracle(orc):
+    rng = np.random.default_rng(5)
+    x = np.concatenate([
+        rng.standard_normal(100003).astype(np.float32),
+        (rng.standard_normal(5000) * 1e-6).astype(np.float32),     # f16 subnormal range
+        (rng.standard_normal(5000) * 7e4).astype(np.float32),      # overflow range
+        np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 65504, 65519.99, 65520, 2 ** -25, -(2 ** -25),
+                  2 ** -24, 1 + 2 ** -11], dtype=np.float32),
+        np.array([0x7F800001, 0xFFC00001, 0x7FBFFFFF, 0x00000001], dtype=np.uint32).view(np.float32),
+    ])
+    want = orc.to_f16(x)
+    for off in (0, 1, 3):           # 16-byte aligned, and not
+        xs = up32(np.concatenate([np.zeros(off, np.float32), x]))[off:]
+        got = f16wm.to_f16(xs)
+        g = got.cpu().numpy().view(np.uint16)
+        assert np.array_equal(g, want), "offset %d: %d differ" % (off, int((g != want).sum()))
+
+
+def test_to_f16_exhaustive(orc):
+    """All 2^32 binary32 bit patterns, bit-exact against the oracle."""
+    chunk = 1 << 27
+    nthreads = min(16, os.cpu_count() or 1)
+    pool = cf.ThreadPoolExecutor(nthreads)
+    bad = 0
+    for c in range((1 << 32) // chunk):
+        lo = c * chunk
+        xg = torch.arange(lo, lo + chunk, dtype=torch.int64, device=DEV).to(torch.int32).view(torch.float32)
+        got = f16wm.to_f16(xg).cpu().numpy().view(np.uint16)
+        xh = np.arange(lo, lo + chunk, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        parts = np.array_split(np.arange(chunk), nthreads)
+        want = np.empty(chunk, dtype=np.uint16)
+
+        def run(ix):
+            want[ix[0]:ix[-1] + 1] = orc.to_f16(xh[ix[0]:ix[-1] + 1])
+        list(pool.map(run, parts))
+        nb = int(np.count_nonzero(got != want))
+        bad += nb
+        if c % 8 == 0 or nb:
+            say("to_f16 exhaustive chunk %d/32: %d mismatches" % (c, nb))
+        del xg
+    pool.shutdown()
+    assert bad == 0
+
+
+# ------------------------------------------------- widening of every f16
+
+def test_every_f16_value_widens_exactly(orc):
+    """Identity weights pick out each activation value: out = widen(a) for all
+    2^16 patterns, through the vec_dot kernels and the tinyBLAS kernel."""
+    k = 1024
+    eye = np.eye(k, dtype=np.float16).view(np.uint16)
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).reshape(64, k)
+    want = orc.widen(pats)
+    w = up16(eye)
+    a = up16(pats)
+    got = f16wm.mat_mul(w, a)                      # n = 64: tinyBLAS order
+    assert_bits_equal(got.cpu().numpy(), want, "widen via tinyBLAS")
+    for c in range(0, 64, 9):                      # one column: vec_dot order
+        got = f16wm.mat_vec(w, a[c])
+        assert_bits_equal(got.cpu().numpy(), want[c], "widen via vec_dot column %d" % c)
+    w13 = up16(eye[:13])
+    got = f16wm.mat_mul(w13, a)                    # rows 13: vec_dot fallback, n columns
+    assert_bits_equal(got.cpu().numpy(), want[:, :13], "widen via fallback")
+
+
+# --------------------------------------------------------------- C1: 576
+
+def test_576_parity_both_orders(orc):
+    """576x576 weight, seed 0: n = 1 (vec_dot) and n = 3 (tinyBLAS), bit-exact,
+    with the activation rounded on the GPU."""
+    w, a = synth.c1()
+    a16_want = orc.to_f16(a)
+    wd = up16(w)
+    a16 = f16wm.to_f16(up32(a))
+    assert np.array_equal(a16.cpu().numpy().view(np.uint16), a16_want)
+    mv = f16wm.mat_vec(wd, a16[0])
+    assert_bits_equal(mv.cpu().numpy(), orc.mat_vec(w, a16_want[0]), "576 n=1")
+    mm = f16wm.mat_mul(wd, a16)
+    want3 = orc.mat_mul(w, a16_want)
+    assert_bits_equal(mm.cpu().numpy(), want3, "576 n=3")
+    # the two orders differ on the GPU exactly where they differ in the oracle
+    per_col = torch.stack([f16wm.mat_vec(wd, a16[c]) for c in range(3)]).cpu().numpy()
+    want_vd = np.stack([orc.mat_vec(w, a16_want[c]) for c in range(3)])
+    assert_bits_equal(per_col, want_vd, "576 vec_dot per column")
+    ndiff = int(np.count_nonzero(per_col.view(np.uint32) != mm.cpu().numpy().view(np.uint32)))
+    say("576x576 n=3: %d of 1728 elements differ between the two orders" % ndiff)
+    assert ndiff == int(np.count_nonzero(want_vd.view(np.uint32) != want3.view(np.uint32))) > 0
+
+
+# ------------------------------------------------ both sides of takes_sgemm
+
+def _sweep_case(orc, rows, k, n, seed, woff=0, aoff=0):
+    w = synth.random_f16((seed, rows, k, 1), (rows, k), 0.02)
+    a = synth.random_f16((seed, rows, k, 2), (n, k))
+    got = f16wm.mat_mul(up16(w, woff), up16(a, aoff))
+    return got, orc.mat_mul(w, a)
+
+
+def test_tail_and_fallback_sweep(orc):
+    """rows 12 and 13 (both sides of rows % 4), every k from 1 to 1,540
+    (every k % 8 and k % 32), n = 1..6: every element bit-exact."""
+    torch.cuda.synchronize()
+    fails = []
+    for rows in (12, 13):
+        for k in range(1, 1541):
+            for n in range(1, 7):
+                got, want = _sweep_case(orc, rows, k, n, 11)
+                g = got.cpu().numpy()
+                if not np.array_equal(g.view(np.uint32), want.view(np.uint32)):
+                    fails.append((rows, k, n))
+        say("sweep rows=%d done, %d failing shapes so far" % (rows, len(fails)))
+    assert not fails, fails[:20]
+
+
+@pytest.mark.parametrize("rows,k,n", [(13, 1540, 2), (12, 1536, 2), (13, 1540, 6), (12, 1536, 6),
+                                      (12, 8, 3), (13, 31, 4), (12, 33, 5), (576, 576, 3),
+                                      (1000, 1000, 5), (100, 4096, 65), (260, 200, 130)])
+@pytest.mark.parametrize("woff,aoff", [(0, 0), (1, 0), (0, 3), (4, 4)])
+def test_shapes_and_alignment(orc, rows, k, n, woff, aoff):
+    """Ragged tiles and misaligned (2-byte) pointers take other kernels; the
+    bits stay the same."""
+    got, want = _sweep_case(orc, rows, k, n, 12, woff, aoff)
+    assert_bits_equal(got.cpu().numpy(), want, "mat_mul %dx%d n=%d offs=%d,%d" % (rows, k, n, woff, aoff))
+    got1 = f16wm.mat_vec(up16(synth.random_f16((12, rows, k, 1), (rows, k), 0.02), woff),
+                         up16(synth.random_f16((12, rows, k, 2), (n, k)), aoff)[0])
+    assert_bits_equal(got1.cpu().numpy(), orc.mat_mul(synth.random_f16((12, rows, k, 1), (rows, k), 0.02),
+                                                      synth.random_f16((12, rows, k, 2), (n, k))[:1])[0],
+                      "mat_vec %dx%d" % (rows, k))
+
+
+# ------------------------------------------------------------ grouped GEMV
+
+@pytest.mark.parametrize("shapes", [
+    [(576, 576), (192, 576), (192, 576)],
+    [(1536, 576), (1536, 576)],
+    [(4096, 4096), (1024, 4096), (1024, 4096)],
+    [(1, 96), (63, 96), (64, 96), (65, 96), (7, 96), (200, 96), (3, 96), (129, 96)],
+    [(5, 33), (7, 33)],
+])
+def test_mat_vec_multi(orc, shapes):
+    k = shapes[0][1]
+    ws = [synth.random_f16((21, i, r, k), (r, k), 0.02) for i, (r, _) in enumerate(shapes)]
+    a = synth.random_f16((22, k), (k,))
+    outs = f16wm.mat_vec_multi([up16(w) for w in ws], up16(a))
+    for i, (w, o) in enumerate(zip(ws, outs)):
+        assert_bits_equal(o.cpu().numpy(), orc.mat_vec(w, a), "multi matrix %d %s" % (i, shapes[i]))
+
+
+# ---------------------------------------------------------- edge cases
+
+def test_degenerate_sizes(orc):
+    w = torch.empty((8, 0), dtype=torch.float16, device=DEV)
+    a = torch.empty((3, 0), dtype=torch.float16, device=DEV)
+    out = torch.full((3, 8), 7.0, device=DEV)
+    f16wm.mat_mul(w, a, out)                                   # k = 0: +0.0 everywhere
+    assert (bits(out) == 0).all()
+    out1 = torch.full((8,), 7.0, device=DEV)
+    f16wm.mat_vec(w, a[0], out1)
+    assert (bits(out1) == 0).all()
+    outm = torch.full((3, 8), 7.0, device=DEV)
+    f16wm.mat_mul_mfma(w, a, outm)
+    assert (bits(outm) == 0).all()
+    # rows = 0 / n = 0: no-ops
+    f16wm.mat_mul(torch.empty((0, 16), dtype=torch.float16, device=DEV),
+                  torch.zeros((2, 16), dtype=torch.float16, device=DEV))
+    f16wm.mat_mul(torch.zeros((4, 16), dtype=torch.float16, device=DEV),
+                  torch.empty((0, 16), dtype=torch.float16, device=DEV))
+    f16wm.to_f16(torch.empty(0, device=DEV))
+
+
+def test_inf_and_nan_propagate_like_the_oracle(orc):
+    rows, k, n = 16, 100, 3
+    w = synth.random_f16(31, (rows, k), 0.02)
+    a = synth.random_f16(32, (n, k))
+    w[2, 5] = 0x7C00      # +inf
+    w[3, 40] = 0xFC00     # -inf
+    w[4, 99] = 0x7E00     # NaN (in the double tail of vec_dot)
+    a[1, 7] = 0x7C00
+    for nn in (1, 2, 3):
+        got = f16wm.mat_mul(up16(w), up16(a[:nn]))
+        assert_bits_equal(got.cpu().numpy(), orc.mat_mul(w, a[:nn]), "inf/nan n=%d" % nn)
+    w2 = synth.random_f16(33, (16, 96), 0.02)
+    w2[1, 3] = 0x7C00
+    w2[1, 4] = 0xFC00      # inf - inf = NaN inside a chain
+    got = f16wm.mat_mul(up16(w2), up16(a[:, :96]))
+    assert_bits_equal(got.cpu().numpy(), orc.mat_mul(w2, a[:, :96]), "inf-inf")
+
+
+def test_large_magnitudes_and_cancellation(orc):
+    """Values near the f16 range limits and heavy cancellation (products up to
+    2^32) exercise every rounding in the trees."""
+    rng = np.random.default_rng(44)
+    for k in (64, 96, 1024, 1027):
+        mag = np.exp2(rng.integers(-24, 16, size=(24, k))).astype(np.float32)
+        sgn = rng.choice([-1.0, 1.0], size=(24, k)).astype(np.float32)
+        w = (mag * sgn).astype(np.float16).view(np.uint16)
+        a = (np.exp2(rng.integers(-24, 16, size=(4, k))) * rng.choice([-1.0, 1.0], size=(4, k))).astype(
+            np.float16).view(np.uint16)
+        for nn in (1, 4):
+            got = f16wm.mat_mul(up16(w), up16(a[:nn]))
+            assert_bits_equal(got.cpu().numpy(), orc.mat_mul(w, a[:nn]), "magnitudes k=%d n=%d" % (k, nn))
+
+
+def test_repeatable_bits():
+    w = up16(synth.random_f16(51, (1000, 4096), 0.02))
+    a = up16(synth.random_f16(52, (7, 4096)))
+    r1 = bits(f16wm.mat_mul(w, a))
+    r2 = bits(f16wm.mat_mul(w, a))
+    assert np.array_equal(r1, r2)
+    v1 = bits(f16wm.mat_vec(w, a[0]))
+    assert np.array_equal(v1, bits(f16wm.mat_vec(w, a[0])))
+
+
+def test_binding_reports_library_errors():
+    w = torch.zeros((4, 12), dtype=torch.float16, device=DEV)
+    a = torch.zeros((3, 12), dtype=torch.float16, device=DEV)
+    with pytest.raises(f16wm.F16WMError) as e:
+        f16wm.mat_mul_mfma(w, a)
+    assert e.value.code == f16wm.F16WM_EUNSUPPORTED
+
+
+# ------------------------------------------------------------ MFMA path
+
+def mfma_error(orc, w, a, got, rr, cc):
+    ref, scale = orc.fp64_at(w, a, rr, cc)
+    y = got[cc, rr].astype(np.float64)
+    err = np.abs(y - ref) / np.maximum(scale, 1e-300)
+    rms = np.sqrt(np.mean(ref ** 2))
+    big = np.abs(ref) >= 1e-2 * rms
+    rel = np.abs(y - ref)[big] / np.abs(ref)[big]
+    return float(err.max()), float(rel.max()) if big.any() else 0.0
+
+
+@pytest.mark.parametrize("rows,k,n", [(128, 32, 128), (200, 40, 130), (576, 576, 512), (1, 8, 1),
+                                      (1000, 4104, 77), (49152, 576, 16)])
+def test_mfma_small_shapes(orc, rows, k, n):
+    w = synth.random_f16((61, rows, k), (rows, k), 0.02)
+    a = synth.random_f16((62, rows, k), (n, k))
+    got = f16wm.mat_mul_mfma(up16(w), up16(a)).cpu().numpy()
+    rng = np.random.default_rng(1)
+    m = min(rows * n, 20000)
+    rr = rng.integers(0, rows, m)
+    cc = rng.integers(0, n, m)
+    e, rel = mfma_error(orc, w, a, got, rr, cc)
+    say("mfma %dx%d n=%d: max err/sum|wa| = %.3g, max rel = %.3g" % (rows, k, n, e, rel))
+    assert e <= MFMA_TOL
+
+
+# ----------------------------------------------- full-size model shapes
+
+def _sample(rows, n, m, seed):
+    rng = np.random.default_rng(seed)
+    rr = np.concatenate([rng.integers(0, rows, m), [0, rows - 1, 0, rows - 1]])
+    cc = np.concatenate([rng.integers(0, n, m), [0, 0, n - 1, n - 1]])
+    return rr, cc
+
+
+def test_smollm2_135m_decode_step_all_matrices(orc):
+    """Every product of a 135M-shaped decode step (30 distinct layers + the tied
+    49152x576 logits), launched as the decode step launches them, bit-exact."""
+    S = synth.SMOLLM2_135M
+    for layer in range(synth.SMOLLM2_135M_LAYERS):
+        ws = {m: synth.weight(synth.CFG_135M, layer, m, *S[m]) for m in S}
+        acts = synth.activation(synth.CFG_135M, layer, 0, 4, 1536)
+        a_attn = orc.to_f16(acts[0, :576])
+        a_o = orc.to_f16(acts[1, :576])
+        a_ffn = orc.to_f16(acts[2, :576])
+        a_down = orc.to_f16(acts[3, :1536])
+        g = {m: up16(ws[m]) for m in ws}
+        q, kk, v = f16wm.mat_vec_multi([g["q"], g["k"], g["v"]], up16(a_attn))
+        o = f16wm.mat_vec(g["o"], up16(a_o))
+        gate, upp = f16wm.mat_vec_multi([g["gate"], g["up"]], up16(a_ffn))
+        down = f16wm.mat_vec(g["down"], up16(a_down))
+        for name, got, w, x in [("q", q, ws["q"], a_attn), ("k", kk, ws["k"], a_attn), ("v", v, ws["v"], a_attn),
+                                ("o", o, ws["o"], a_o), ("gate", gate, ws["gate"], a_ffn),
+                                ("up", upp, ws["up"], a_ffn), ("down", down, ws["down"], a_down)]:
+            assert_bits_equal(got.cpu().numpy(), orc.mat_vec(w, x), "135M layer %d %s" % (layer, name))
+        if layer % 10 == 0:
+            say("135M decode layer %d ok" % layer)
+    wl = synth.weight(synth.CFG_135M, 0, "logits", *synth.SMOLLM2_135M_LOGITS)
+    al = orc.to_f16(synth.activation(synth.CFG_135M, 30, 0, 1, 576)[0])
+    got = f16wm.mat_vec(up16(wl), up16(al))
+    assert_bits_equal(got.cpu().numpy(), orc.mat_vec(wl, al), "135M logits")
+
+
+def test_smollm2_135m_prefill_512(orc):
+    """n = 512 micro-batch on the 135M matrices (tinyBLAS order): layer 0 in
+    full, the logits on sampled elements; MFMA within tolerance."""
+    S = synth.SMOLLM2_135M
+    acts = synth.activation(synth.CFG_135M_PREFILL, 0, 0, synth.PREFILL_N, 1536)
+    for m, (rows, k) in S.items():
+        w = synth.weight(synth.CFG_135M, 0, m, rows, k)
+        a16 = orc.to_f16(acts[:, :k])
+        got = f16wm.mat_mul(up16(w), up16(a16)).cpu().numpy()
+        assert_bits_equal(got, orc.mat_mul(w, a16), "135M prefill layer 0 %s" % m)
+        gm = f16wm.mat_mul_mfma(up16(w), up16(a16)).cpu().numpy()
+        rr, cc = _sample(rows, synth.PREFILL_N, 4000, 3)
+        e, _ = mfma_error(orc, w, a16, gm, rr, cc)
+        say("135M prefill %s exact ok; mfma err %.3g" % (m, e))
+        assert e <= MFMA_TOL
+    wl = synth.weight(synth.CFG_135M, 0, "logits", *synth.SMOLLM2_135M_LOGITS)
+    a16 = orc.to_f16(acts[:, :576])
+    got = f16wm.mat_mul(up16(wl), up16(a16)).cpu().numpy()
+    rr, cc = _sample(wl.shape[0], synth.PREFILL_N, 20000, 4)
+    assert_bits_equal(got[cc, rr], orc.mat_mul_at(wl, a16, rr, cc), "135M prefill logits (sampled)")
+
+
+def test_llama3_8b_decode_gemv_all_matrices(orc):
+    """The 8B-shaped GEMV set at full size, launched as the benchmark launches
+    it (Q/K/V and gate/up grouped), every element bit-exact."""
+    S = synth.LLAMA3_8B
+    ws = {m: synth.weight(synth.CFG_8B, 0, m, *S[m]) for m in S}
+    ws["logits"] = synth.weight(synth.CFG_8B, 0, "logits", *synth.LLAMA3_8B_LOGITS)
+    acts = synth.activation(synth.CFG_8B, 0, 0, 5, 14336)
+    x = {"attn": orc.to_f16(acts[0, :4096]), "o": orc.to_f16(acts[1, :4096]),
+         "ffn": orc.to_f16(acts[2, :4096]), "down": orc.to_f16(acts[3, :14336]),
+         "logits": orc.to_f16(acts[4, :4096])}
+    g = {m: up16(w) for m, w in ws.items()}
+    q, kk, v = f16wm.mat_vec_multi([g["q"], g["k"], g["v"]], up16(x["attn"]))
+    gate, upp = f16wm.mat_vec_multi([g["gate"], g["up"]], up16(x["ffn"]))
+    res = {"q": (q, "attn"), "k": (kk, "attn"), "v": (v, "attn"), "gate": (gate, "ffn"), "up": (upp, "ffn"),
+           "o": (f16wm.mat_vec(g["o"], up16(x["o"])), "o"),
+           "down": (f16wm.mat_vec(g["down"], up16(x["down"])), "down"),
+           "logits": (f16wm.mat_vec(g["logits"], up16(x["logits"])), "logits")}
+    for m, (got, src) in res.items():
+        assert_bits_equal(got.cpu().numpy(), orc.mat_vec(ws[m], x[src]), "8B gemv %s" % m)
+        say("8B gemv %s ok" % m)
+
+
+def test_llama3_8b_prefill_512(orc):
+    """n = 512 on the 8B matrices: exact order on sampled elements (the oracle
+    would need minutes for all 3.8e11 FMAs), MFMA within tolerance."""
+    S = dict(synth.LLAMA3_8B)
+    S["logits"] = synth.LLAMA3_8B_LOGITS
+    acts = synth.activation(synth.CFG_8B_PREFILL, 0, 0, synth.PREFILL_N, 14336)
+    for i, (m, (rows, k)) in enumerate(S.items()):
+        w = synth.weight(synth.CFG_8B, 0, m, rows, k)
+        a16 = orc.to_f16(acts[:, :k])
+        wd, ad = up16(w), up16(a16)
+        got = f16wm.mat_mul(wd, ad).cpu().numpy()
+        rr, cc = _sample(rows, synth.PREFILL_N, 3000, 10 + i)
+        assert_bits_equal(got[cc, rr], orc.mat_mul_at(w, a16, rr, cc), "8B prefill %s (sampled)" % m)
+        gm = f16wm.mat_mul_mfma(wd, ad).cpu().numpy()
+        e, rel = mfma_error(orc, w, a16, gm, rr, cc)
+        say("8B prefill %s: exact ok; mfma err %.3g rel %.3g" % (m, e, rel))
+        assert e <= MFMA_TOL
+        del wd, ad
