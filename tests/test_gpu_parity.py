@@ -121,22 +121,32 @@ def test_to_f16_exhaustive(orc):
 # ------------------------------------------------- widening of every f16
 
 def test_every_f16_value_widens_exactly(orc):
-    """Identity weights pick out each activation value: out = widen(a) for all
-    2^16 patterns, through the vec_dot kernels and the tinyBLAS kernel."""
-    k = 1024
-    eye = np.eye(k, dtype=np.float16).view(np.uint16)
-    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).reshape(64, k)
-    want = orc.widen(pats)
-    w = up16(eye)
-    a = up16(pats)
-    got = f16wm.mat_mul(w, a)                      # n = 64: tinyBLAS order
-    assert_bits_equal(got.cpu().numpy(), want, "widen via tinyBLAS")
-    for c in range(0, 64, 9):                      # one column: vec_dot order
-        got = f16wm.mat_vec(w, a[c])
-        assert_bits_equal(got.cpu().numpy(), want[c], "widen via vec_dot column %d" % c)
-    w13 = up16(eye[:13])
-    got = f16wm.mat_mul(w13, a)                    # rows 13: vec_dot fallback, n columns
-    assert_bits_equal(got.cpu().numpy(), want[:, :13], "widen via fallback")
+    """Every one of the 2^16 f16 patterns goes through each kernel's widening:
+    each activation column holds one pattern next to zeros and the weight
+    rows are one-hot on it, so the product is widen(pattern) (exactly; NaN as
+    NaN).  Bit-exact against the oracle, and equal to the oracle's widen on
+    every non-NaN pattern."""
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    wid = orc.widen(pats)
+    for rows, k, what in [(4, 8, "tinyBLAS"), (3, 32, "vec_dot fallback (n columns)"),
+                          (4, 33, "vec_dot, double tail")]:
+        w = np.zeros((rows, k), dtype=np.uint16)
+        w[:, 0] = 0x3C00                                   # 1.0
+        if k == 33:
+            w[:, 0], w[:, 32] = 0, 0x3C00                   # the pattern sits in the tail
+        a = np.zeros((pats.size, k), dtype=np.uint16)
+        a[:, 32 if k == 33 else 0] = pats
+        got = f16wm.mat_mul(up16(w), up16(a)).cpu().numpy()      # n = 65536 columns
+        assert_bits_equal(got, orc.mat_mul(w, a), "widen via " + what)
+        ok = ~np.isnan(wid) & (pats != 0x8000)             # -0 * 1 + (+0) = +0
+        assert np.array_equal(got[ok, 0].view(np.uint32), wid[ok].view(np.uint32)), what
+    # one column at a time through the GEMV kernel
+    w = np.zeros((4, 64), dtype=np.uint16)
+    w[np.arange(4), np.arange(4) * 9] = 0x3C00
+    for c0 in range(0, 1 << 16, 64 * 97):
+        col = pats[c0:c0 + 64].copy()
+        got = f16wm.mat_vec(up16(w), up16(col)).cpu().numpy()
+        assert_bits_equal(got, orc.mat_vec(w, col), "widen via vec_dot GEMV at %d" % c0)
 
 
 # --------------------------------------------------------------- C1: 576
