@@ -66,49 +66,173 @@ __device__ __forceinline__ float add_tail(float v, const uint16_t *w, const uint
     return (float)d;
 }
 
-constexpr int kV8Rows = 64;   // rows per 256-thread block, 4 lanes per row
-constexpr int kV8Batch = 8;   // 32-element steps loaded ahead of their FMAs
-
-__global__ __launch_bounds__(256) void vec_dot_v8(RowTable t, int64_t k,
-                                                  const uint16_t *__restrict__ a_all)
+// The 32 chains of one element, spread over LPR lanes (CPL = 32 / LPR chains
+// per lane: global chain c = CPL*j + i for lane j, register i), reduced in the
+// vec_dot tree: c with c^16 and c^8 ((a0+a2)+(a1+a3)), c^4 (low + high half),
+// c^1 then c^2 (the two horizontal adds).  A pairing across lanes is a shuffle
+// by (bit / CPL); a pairing inside a lane adds two registers.  The result is
+// in register 0 of every lane of the row.
+template <int CPL>
+__device__ __forceinline__ float vec_dot_tree(float (&v)[CPL])
 {
+    constexpr int kBits[5] = {16, 8, 4, 1, 2};
+#pragma unroll
+    for (int L = 0; L < 5; L++) {
+        const int b = kBits[L];
+        if (b >= CPL) {
+#pragma unroll
+            for (int i = 0; i < CPL; i++) v[i] = v[i] + __shfl_xor(v[i], b / CPL);
+        } else {
+#pragma unroll
+            for (int i = 0; i < CPL; i++)
+                if ((i & b) == 0) v[i] = v[i] + v[i | b];
+        }
+    }
+    return v[0];
+}
+
+template <int N>
+struct Halves;
+template <>
+struct Halves<8> { typedef u32x4 T; };
+template <>
+struct Halves<4> { typedef uint2 T; };
+template <>
+struct Halves<2> { typedef uint32_t T; };
+template <>
+struct Halves<1> { typedef uint16_t T; };
+
+// acc[i] = fma(w_i, a_i, acc[i]) for the CPL f16 pairs packed in w and a.
+template <int CPL>
+__device__ __forceinline__ void fma_halves(float (&acc)[CPL], typename Halves<CPL>::T w,
+                                           typename Halves<CPL>::T a)
+{
+    typedef _Float16 hv __attribute__((ext_vector_type(CPL == 1 ? 2 : CPL)));
+    if constexpr (CPL == 1) {
+        acc[0] = __builtin_fmaf(widen(w), widen(a), acc[0]);
+    } else {
+        const hv wh = __builtin_bit_cast(hv, w);
+        const hv ah = __builtin_bit_cast(hv, a);
+#pragma unroll
+        for (int i = 0; i < CPL; i++) acc[i] = __builtin_fmaf((float)wh[i], (float)ah[i], acc[i]);
+    }
+}
+
+// LDS-staged GEMV for k % 8 == 0 and 16-byte aligned rows.
+//
+// A 256-thread block owns R = 256 / LPR rows.  Each stage copies SC elements
+// of every row (32 KB of weights) plus the matching SC activation elements
+// from HBM into LDS with 16-byte loads in which consecutive lanes read
+// consecutive bytes of one row (512 B to 4 KB contiguous per row), so every
+// wave load is fully coalesced.  The compute lanes then read their chains'
+// elements from LDS: lane j of a row owns chains CPL*j .. CPL*j + CPL - 1 and
+// per 32-element step reads CPL consecutive halves of the row and of the
+// activation.  Two LDS buffers: the next stage's loads are in flight while
+// the current stage computes.  Rows are padded to a stride of 64 mod 256
+// bytes so the rows read by one LDS instruction fall in different banks.
+template <int LPR>
+struct LdsCfg {
+    static constexpr int R = 256 / LPR;        // rows per block
+    static constexpr int CPL = 32 / LPR;       // chains per lane
+    static constexpr int SC = 16384 / R;       // elements per row per stage
+    static constexpr int U = SC / 8;           // 16-byte units per row per stage
+    static constexpr int UPT = R * U / 256;    // units per thread per stage
+    static constexpr int ROWB = SC * 2 + 64;   // LDS row stride, bytes
+    static constexpr int WBYTES = R * ROWB;    // weight bytes per LDS buffer
+    static constexpr int BUFB = WBYTES + SC * 2;
+};
+
+template <int LPR>
+__global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k,
+                                                   const uint16_t *__restrict__ a_all)
+{
+    typedef LdsCfg<LPR> C;
+    typedef typename Halves<C::CPL>::T HT;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * C::BUFB];
+
+    const int tid = threadIdx.x;
     const int64_t col = blockIdx.y;
     const uint16_t *a = a_all + col * k;
-    const int q = threadIdx.x & 3;
-    const int64_t g = (int64_t)blockIdx.x * kV8Rows + (threadIdx.x >> 2);
-    const bool valid = g < t.row0[t.count];
-    const int m = find_matrix(t, valid ? g : 0);
-    const int64_t r = valid ? g - t.row0[m] : 0;
-    const uint16_t *wrow = t.w[m] + r * k;
-    const int64_t nsteps = k >> 5;
+    const int64_t total = t.row0[t.count];
+    const int64_t g0 = (int64_t)blockIdx.x * C::R;
 
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (valid) {
-        const u32x4 *wp = reinterpret_cast<const u32x4 *>(wrow) + q;
-        const u32x4 *ap = reinterpret_cast<const u32x4 *>(a) + q;
-        int64_t s = 0;
-        for (; s + kV8Batch <= nsteps; s += kV8Batch) {
-            u32x4 wv[kV8Batch], av[kV8Batch];
+    // Source rows of this thread's stage units (the same rows every stage).
+    const uint16_t *src[C::UPT];
 #pragma unroll
-            for (int u = 0; u < kV8Batch; u++) {
-                wv[u] = __builtin_nontemporal_load(wp + 4 * (s + u));
-                av[u] = ap[4 * (s + u)];
-            }
-#pragma unroll
-            for (int u = 0; u < kV8Batch; u++) fma8(acc, wv[u], av[u]);
+    for (int p = 0; p < C::UPT; p++) {
+        const int f = p * 256 + tid;
+        const int64_t g = g0 + f / C::U;
+        src[p] = nullptr;
+        if (g < total) {
+            const int m = find_matrix(t, g);
+            src[p] = t.w[m] + (g - t.row0[m]) * k + 8 * (f % C::U);
         }
-        for (; s < nsteps; s++) fma8(acc, __builtin_nontemporal_load(wp + 4 * s), ap[4 * s]);
     }
-    // (a0 + a2) and (a1 + a3), then their sum: partners q^2, then q^1.
-#pragma unroll
-    for (int l = 0; l < 8; l++) acc[l] = acc[l] + __shfl_xor(acc[l], 2);
-#pragma unroll
-    for (int l = 0; l < 8; l++) acc[l] = acc[l] + __shfl_xor(acc[l], 1);
+    const bool act_loader = tid < C::U;
+    const uint16_t *asrc = a + 8 * tid;
 
-    if (valid && q == 0) {
-        const float u0 = acc[0] + acc[4], u1 = acc[1] + acc[5];   // low + high half
-        const float u2 = acc[2] + acc[6], u3 = acc[3] + acc[7];
-        float v = (u0 + u1) + (u2 + u3);                          // two horizontal adds
+    const int64_t nsteps = k >> 5;                       // full 32-element steps
+    const int64_t nstages = (k + C::SC - 1) / C::SC;
+
+    u32x4 wreg[C::UPT];
+    u32x4 areg;
+    auto fetch = [&](int64_t s) {
+        const int64_t k0 = s * C::SC;
+#pragma unroll
+        for (int p = 0; p < C::UPT; p++) {
+            const int f = p * 256 + tid;
+            if (src[p] && k0 + 8 * (f % C::U) < k)
+                wreg[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src[p] + k0));
+        }
+        if (act_loader && k0 + 8 * tid < k) areg = *reinterpret_cast<const u32x4 *>(asrc + k0);
+    };
+    auto stash = [&](int buf) {
+        unsigned char *base = lds + buf * C::BUFB;
+#pragma unroll
+        for (int p = 0; p < C::UPT; p++) {
+            const int f = p * 256 + tid;
+            *reinterpret_cast<u32x4 *>(base + (f / C::U) * C::ROWB + 16 * (f % C::U)) = wreg[p];
+        }
+        if (act_loader) *reinterpret_cast<u32x4 *>(base + C::WBYTES + 16 * tid) = areg;
+    };
+
+    const int rho = tid / LPR;
+    const int j = tid % LPR;
+    float acc[C::CPL];
+#pragma unroll
+    for (int i = 0; i < C::CPL; i++) acc[i] = 0.f;
+
+    if (nstages > 0) {
+        fetch(0);
+        stash(0);
+    }
+    __syncthreads();
+    for (int64_t s = 0; s < nstages; s++) {
+        const int buf = (int)(s & 1);
+        if (s + 1 < nstages) fetch(s + 1);
+        const unsigned char *wl = lds + buf * C::BUFB + rho * C::ROWB + j * C::CPL * 2;
+        const unsigned char *al = lds + buf * C::BUFB + C::WBYTES + j * C::CPL * 2;
+        const int64_t left = nsteps - s * (C::SC / 32);
+        if (left >= C::SC / 32) {
+#pragma unroll 8
+            for (int st = 0; st < C::SC / 32; st++)
+                fma_halves<C::CPL>(acc, *reinterpret_cast<const HT *>(wl + 64 * st),
+                                   *reinterpret_cast<const HT *>(al + 64 * st));
+        } else {
+            for (int st = 0; st < (int)left; st++)
+                fma_halves<C::CPL>(acc, *reinterpret_cast<const HT *>(wl + 64 * st),
+                                   *reinterpret_cast<const HT *>(al + 64 * st));
+        }
+        if (s + 1 < nstages) stash(buf ^ 1);
+        __syncthreads();
+    }
+
+    float v = vec_dot_tree<C::CPL>(acc);
+    const int64_t g = g0 + rho;
+    if (j == 0 && g < total) {
+        const int m = find_matrix(t, g);
+        const int64_t r = g - t.row0[m];
+        const uint16_t *wrow = t.w[m] + r * k;
         if (k & 31) v = add_tail(v, wrow, a, nsteps * 32, k);
         const int64_t rows_m = t.row0[m + 1] - t.row0[m];
         t.out[m][col * rows_m + r] = v;
@@ -156,20 +280,35 @@ hipError_t launch_vec_dot(const RowTable &t, int64_t k, const uint16_t *a, int64
                           hipStream_t stream)
 {
     const int64_t total = t.row0[t.count];
-    const int per = vec8 ? kV8Rows : kV1Rows;
+    // Lanes per row: the fewest (most chains per lane) that still give at
+    // least two blocks per CU (512 blocks) for this many rows.
+    int lpr = 32;
+    if (vec8) {
+        if (total >= 512 * 64) lpr = 4;
+        else if (total >= 512 * 32) lpr = 8;
+        else if (total >= 512 * 16) lpr = 16;
+    }
+    const int per = vec8 ? 256 / lpr : kV1Rows;
     const int64_t bx = (total + per - 1) / per;
+    if (bx > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
     // grid.y is limited to 65535: launch column chunks, each with its own
     // activation and output offsets.
-    if (bx > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
     for (int64_t c0 = 0; c0 < ncols; c0 += 65535) {
         const int64_t nc = ncols - c0 < 65535 ? ncols - c0 : 65535;
         RowTable tc = t;
         for (int i = 0; i < t.count; i++) tc.out[i] = t.out[i] + c0 * (t.row0[i + 1] - t.row0[i]);
         const dim3 grid((uint32_t)bx, (uint32_t)nc);
-        if (vec8)
-            vec_dot_v8<<<grid, dim3(256), 0, stream>>>(tc, k, a + c0 * k);
+        const uint16_t *ac = a + c0 * k;
+        if (!vec8)
+            vec_dot_v1<<<grid, dim3(256), 0, stream>>>(tc, k, ac);
+        else if (lpr == 4)
+            vec_dot_lds<4><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
+        else if (lpr == 8)
+            vec_dot_lds<8><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
+        else if (lpr == 16)
+            vec_dot_lds<16><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
         else
-            vec_dot_v1<<<grid, dim3(256), 0, stream>>>(tc, k, a + c0 * k);
+            vec_dot_lds<32><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
