@@ -13,9 +13,17 @@
 // 32 lanes holding one output register cover 32 consecutive r: the stores to
 // out[c*rows + r] are coalesced.
 //
-// 256-thread block, 128 (c) x 128 (r) tile, 2 x 2 waves of 64 x 64 (2 x 2 MFMA
-// 32x32 tiles each), k staged 32 at a time through padded LDS rows (80-byte
-// stride: conflict-free 16-byte reads), next stage prefetched into registers.
+// Tiling: a 256-thread block computes BM columns x BN rows as 2 x 2 waves;
+// each wave owns (BM/2) x (BN/2) = TM x TN MFMA tiles of 32 x 32.  With
+// 128 x 128 per wave (16 tiles, 256 accumulators in AGPRs) every 16-byte LDS
+// fragment feeds four MFMAs, which keeps LDS reads at half the LDS bandwidth.
+// k is staged 32 at a time through two LDS buffers with 80-byte rows (a
+// stride that puts the 16 rows of one LDS read phase in 16 different bank
+// groups); the global loads of the next three stages are in flight during
+// the MFMAs (weights come from HBM with microseconds of latency).
+// Block b runs on XCD b % 8; tiles are handed out so each XCD walks a
+// contiguous range, and consecutive tiles share one weight-row block, so its
+// weights are read from HBM once and re-read from that XCD's L2.
 #include "kernels.h"
 
 namespace f16wm {
@@ -25,95 +33,157 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMB = 128;         // activation columns per block
-constexpr int kNB = 128;         // weight rows per block
-constexpr int kKB = 32;          // k per stage
-constexpr int kLD = kKB + 8;     // padded LDS row, in halves
+constexpr int kKS = 32;          // k per stage
+constexpr int kLD = kKS + 8;     // padded LDS row, in halves (80 bytes)
 
+template <int BM, int BN>
 __global__ __launch_bounds__(256) void mfma_kernel(const uint16_t *__restrict__ w, int64_t rows,
                                                    int64_t k, const uint16_t *__restrict__ a,
-                                                   int64_t n, float *__restrict__ out)
+                                                   int64_t n, float *__restrict__ out, int nrt,
+                                                   int nct)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t As[kMB][kLD];
-    __shared__ __attribute__((aligned(16))) uint16_t Ws[kNB][kLD];
+    constexpr int WM = BM / 2, WN = BN / 2;       // wave tile
+    constexpr int TM = WM / 32, TN = WN / 32;     // 32x32 MFMA tiles per wave
+    constexpr int AUPT = BM * kKS / 8 / 256;      // 16-byte activation units per thread
+    constexpr int WUPT = BN * kKS / 8 / 256;      // 16-byte weight units per thread
+    static_assert(AUPT >= 1 && WUPT >= 1, "tile too small for 256 threads");
+
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][kLD];
+    __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN][kLD];
+
+    // XCD-aware tile index (blocks are dispatched round-robin over 8 XCDs).
+    const int ntiles = nrt * nct;
+    const int b = blockIdx.x;
+    const int xcd = b & 7, pos = b >> 3, q = ntiles >> 3, rem = ntiles & 7;
+    const int t = xcd * q + (xcd < rem ? xcd : rem) + pos;
+    const int64_t r0 = (int64_t)(t / nct) * BN;
+    const int64_t c0 = (int64_t)(t % nct) * BM;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1;        // columns wm*64 .. +63 of the tile
-    const int wn = wave & 1;         // rows    wn*64 .. +63 of the tile
-    const int64_t r0 = (int64_t)blockIdx.x * kNB;
-    const int64_t c0 = (int64_t)blockIdx.y * kMB;
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-#pragma unroll
-            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
-
-    u32x4 areg[2], wreg[2];
-#define F16WM_MFMA_FETCH(K0)                                                                  \
-    do {                                                                                      \
-        _Pragma("unroll") for (int p = 0; p < 2; p++) {                                       \
-            const int idx = tid + 256 * p;                                                    \
-            const int row = idx >> 2, kv = idx & 3;                                           \
-            const int64_t gk = (K0) + kv * 8;                                                 \
-            const int64_t gc = c0 + row, gr = r0 + row;                                       \
-            u32x4 av = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};                               \
-            if (gc < n && gk < k) av = *reinterpret_cast<const u32x4 *>(a + gc * k + gk);     \
-            if (gr < rows && gk < k) wv = *reinterpret_cast<const u32x4 *>(w + gr * k + gk);  \
-            areg[p] = av;                                                                     \
-            wreg[p] = wv;                                                                     \
-        }                                                                                     \
-    } while (0)
-
+    const int wm = wave >> 1;         // columns wm*WM .. of the tile
+    const int wn = wave & 1;          // rows    wn*WN .. of the tile
     const int lr = lane & 31;         // operand row within a 32-row block
     const int lk = (lane >> 5) * 8;   // k offset of the lane's 8 values
 
-    if (k > 0) F16WM_MFMA_FETCH(0);
-    for (int64_t k0 = 0; k0 < k; k0 += kKB) {
-        __syncthreads();
+    f32x16 acc[TM][TN];
 #pragma unroll
-        for (int p = 0; p < 2; p++) {
-            const int idx = tid + 256 * p;
-            const int row = idx >> 2, kv = idx & 3;
-            *reinterpret_cast<u32x4 *>(&As[row][kv * 8]) = areg[p];
-            *reinterpret_cast<u32x4 *>(&Ws[row][kv * 8]) = wreg[p];
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+
+    // Global loads are issued for stage s + 3 while stage s computes; stage s
+    // waits in register set s % 3 until it is copied into LDS buffer s % 2.
+    // Every load is issued unconditionally from a clamped, valid address and
+    // out-of-range values are replaced by zero when copied to LDS, so the loop
+    // has no branches and the compiler can wait for exactly the oldest stage.
+    // The stage count is rounded up to a multiple of 3; the extra stages are
+    // all zeros and add nothing.
+    u32x4 areg[3][AUPT], wreg[3][WUPT];
+    const int64_t nstages = (k + kKS - 1) / kKS;
+    const int64_t last_k = k >= 8 ? k - 8 : 0;
+    auto fetch = [&](int64_t s, int set) {
+        const int64_t k0 = s * kKS;
+#pragma unroll
+        for (int p = 0; p < AUPT; p++) {
+            const int idx = p * 256 + tid;
+            const int64_t gk = k0 + (idx & 3) * 8, gc = c0 + (idx >> 2);
+            const int64_t ck = gk < k ? gk : last_k, cc = gc < n ? gc : n - 1;
+            areg[set][p] = *reinterpret_cast<const u32x4 *>(a + cc * k + ck);
         }
-        __syncthreads();
-        if (k0 + kKB < k) F16WM_MFMA_FETCH(k0 + kKB);
 #pragma unroll
-        for (int kk = 0; kk < kKB; kk += 16) {
-            half8 af[2], bf[2];
+        for (int p = 0; p < WUPT; p++) {
+            const int idx = p * 256 + tid;
+            const int64_t gk = k0 + (idx & 3) * 8, gr = r0 + (idx >> 2);
+            const int64_t ck = gk < k ? gk : last_k, cr = gr < rows ? gr : rows - 1;
+            wreg[set][p] = *reinterpret_cast<const u32x4 *>(w + cr * k + ck);
+        }
+    };
+    auto stash = [&](int64_t s, int set, int buf) {
+        const int64_t k0 = s * kKS;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int i = 0; i < 2; i++)
-                af[i] = *reinterpret_cast<const half8 *>(&As[wm * 64 + i * 32 + lr][kk + lk]);
+        for (int p = 0; p < AUPT; p++) {
+            const int idx = p * 256 + tid;
+            const bool ok = k0 + (idx & 3) * 8 < k && c0 + (idx >> 2) < n;
+            *reinterpret_cast<u32x4 *>(&As[buf][idx >> 2][(idx & 3) * 8]) = ok ? areg[set][p] : zero;
+        }
 #pragma unroll
-            for (int j = 0; j < 2; j++)
-                bf[j] = *reinterpret_cast<const half8 *>(&Ws[wn * 64 + j * 32 + lr][kk + lk]);
+        for (int p = 0; p < WUPT; p++) {
+            const int idx = p * 256 + tid;
+            const bool ok = k0 + (idx & 3) * 8 < k && r0 + (idx >> 2) < rows;
+            *reinterpret_cast<u32x4 *>(&Ws[buf][idx >> 2][(idx & 3) * 8]) = ok ? wreg[set][p] : zero;
+        }
+    };
+    auto compute = [&](int buf) {
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+        for (int kk = 0; kk < kKS; kk += 16) {
+            half8 af[TM], bf[TN];
 #pragma unroll
-                for (int j = 0; j < 2; j++)
+            for (int i = 0; i < TM; i++)
+                af[i] = *reinterpret_cast<const half8 *>(&As[buf][wm * WM + i * 32 + lr][kk + lk]);
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+                bf[j] = *reinterpret_cast<const half8 *>(&Ws[buf][wn * WN + j * 32 + lr][kk + lk]);
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    if (nstages > 0) {
+        const int64_t S = (nstages + 2) / 3 * 3;
+        fetch(0, 0);
+        fetch(1, 1);
+        fetch(2, 2);
+        stash(0, 0, 0);
+        __syncthreads();
+        for (int64_t s = 0; s < S; s += 3) {
+            const int b0 = (int)(s & 1);     // LDS buffer of stage s
+            fetch(s + 3, 0);
+            compute(b0);
+            stash(s + 1, 1, b0 ^ 1);
+            __syncthreads();
+            fetch(s + 4, 1);
+            compute(b0 ^ 1);
+            stash(s + 2, 2, b0);
+            __syncthreads();
+            fetch(s + 5, 2);
+            compute(b0);
+            stash(s + 3, 0, b0 ^ 1);
+            __syncthreads();
         }
     }
 
     // D[i][j] of a 32x32 tile sits in lane j + 32*((i/4)%2), register (i%4) + 4*(i/8).
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < TM; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int64_t r = r0 + wn * 64 + j * 32 + lr;
+        for (int j = 0; j < TN; j++) {
+            const int64_t r = r0 + wn * WN + j * 32 + lr;
 #pragma unroll
             for (int v = 0; v < 16; v++) {
-                const int64_t c = c0 + wm * 64 + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+                const int64_t c = c0 + wm * WM + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
                 if (r < rows && c < n) out[c * rows + r] = acc[i][j][v];
             }
         }
-#undef F16WM_MFMA_FETCH
+}
+
+template <int BM, int BN>
+hipError_t launch_tiles(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
+                        float *out, hipStream_t stream)
+{
+    const int64_t nrt = (rows + BN - 1) / BN;
+    const int64_t nct = (n + BM - 1) / BM;
+    if (nrt * nct > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
+    mfma_kernel<BM, BN><<<dim3((uint32_t)(nrt * nct)), dim3(256), 0, stream>>>(w, rows, k, a, n, out,
+                                                                           (int)nrt, (int)nct);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -121,19 +191,11 @@ __global__ __launch_bounds__(256) void mfma_kernel(const uint16_t *__restrict__ 
 hipError_t launch_mfma(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
                        float *out, hipStream_t stream)
 {
-    const int64_t bx = (rows + kNB - 1) / kNB;
-    const int64_t by_all = (n + kMB - 1) / kMB;
-    if (bx > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
-    for (int64_t b0 = 0; b0 < by_all; b0 += 65535) {
-        const int64_t by = by_all - b0 < 65535 ? by_all - b0 : 65535;
-        const int64_t c0 = b0 * kMB;
-        const int64_t nc = n - c0 < by * kMB ? n - c0 : by * kMB;
-        mfma_kernel<<<dim3((uint32_t)bx, (uint32_t)by), dim3(256), 0, stream>>>(
-            w, rows, k, a + c0 * k, nc, out + c0 * rows);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    // 256 x 256 tiles when they still give at least one block per CU,
+    // 128 x 128 otherwise.
+    const int64_t big = ((rows + 255) / 256) * ((n + 255) / 256);
+    if (big >= 256) return launch_tiles<256, 256>(w, rows, k, a, n, out, stream);
+    return launch_tiles<128, 128>(w, rows, k, a, n, out, stream);
 }
 
 }  // namespace f16wm

@@ -121,7 +121,7 @@ __device__ __forceinline__ void fma_halves(float (&acc)[CPL], typename Halves<CP
 // LDS-staged GEMV for k % 8 == 0 and 16-byte aligned rows.
 //
 // A 256-thread block owns R = 256 / LPR rows.  Each stage copies SC elements
-// of every row (32 KB of weights) plus the matching SC activation elements
+// of every row (16 or 32 KB of weights) plus the matching SC activation elements
 // from HBM into LDS with 16-byte loads in which consecutive lanes read
 // consecutive bytes of one row (512 B to 4 KB contiguous per row), so every
 // wave load is fully coalesced.  The compute lanes then read their chains'
@@ -134,12 +134,17 @@ template <int LPR>
 struct LdsCfg {
     static constexpr int R = 256 / LPR;        // rows per block
     static constexpr int CPL = 32 / LPR;       // chains per lane
-    static constexpr int SC = 16384 / R;       // elements per row per stage
+    // Weight bytes per stage: 32 KB for the 64-row blocks, 16 KB otherwise
+    // (measured best on MI355X for tall matrices and for 4k-14k rows).
+    static constexpr int STAGE = LPR == 4 ? 32768 : 16384;
+    static constexpr int SC = STAGE / 2 / R;   // elements per row per stage
     static constexpr int U = SC / 8;           // 16-byte units per row per stage
     static constexpr int UPT = R * U / 256;    // units per thread per stage
     static constexpr int ROWB = SC * 2 + 64;   // LDS row stride, bytes
     static constexpr int WBYTES = R * ROWB;    // weight bytes per LDS buffer
     static constexpr int BUFB = WBYTES + SC * 2;
+    static_assert(U <= 256, "one 16-byte activation unit per thread per stage");
+    static_assert(R * U % 256 == 0, "whole units per thread");
 };
 
 template <int LPR>
@@ -280,12 +285,12 @@ hipError_t launch_vec_dot(const RowTable &t, int64_t k, const uint16_t *a, int64
                           hipStream_t stream)
 {
     const int64_t total = t.row0[t.count];
-    // Lanes per row: the fewest (most chains per lane) that still give at
-    // least two blocks per CU (512 blocks) for this many rows.
+    // Lanes per row: 4 (64-row blocks) when that still gives two blocks per
+    // CU, else 16 when that does, else 32 (measured on the 8B shapes; 8
+    // lanes per row was never faster).
     int lpr = 32;
     if (vec8) {
         if (total >= 512 * 64) lpr = 4;
-        else if (total >= 512 * 32) lpr = 8;
         else if (total >= 512 * 16) lpr = 16;
     }
     const int per = vec8 ? 256 / lpr : kV1Rows;
