@@ -37,7 +37,7 @@ constexpr int kKS = 32;          // k per stage
 constexpr int kLD = kKS + 8;     // padded LDS row, in halves (80 bytes)
 
 template <int BM, int BN>
-__global__ __launch_bounds__(256) void mfma_kernel(const uint16_t *__restrict__ w, int64_t rows,
+__global__ __launch_bounds__(256) void mfma_generic(const uint16_t *__restrict__ w, int64_t rows,
                                                    int64_t k, const uint16_t *__restrict__ a,
                                                    int64_t n, float *__restrict__ out, int nrt,
                                                    int nct)
@@ -174,6 +174,151 @@ __global__ __launch_bounds__(256) void mfma_kernel(const uint16_t *__restrict__ 
         }
 }
 
+// Fast path: k % 64 == 0.  Same tiling and MFMA order as mfma_generic, with
+//  - buffer loads: each block addresses its activation and weight tiles
+//    through buffer resources whose size ends at the tile's last valid row,
+//    so rows past the matrix read as zero without a branch, and the prefetch
+//    running past the last stage reads zero (offset past the resource end);
+//  - 64-element k stages, two register sets (stages s+1 and s+2 in flight);
+//  - unpadded 128-byte LDS rows with the 16-byte chunk index XORed by
+//    (row / 2) % 8, which keeps both the row-wise stores and the 16-rows-per-
+//    phase fragment reads free of bank conflicts.
+constexpr int kFKS = 64;   // k per stage
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base, int64_t bytes)
+{
+    // raw buffer: stride 0, num_records = bytes, gfx9 dword3
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void mfma_fast(const uint16_t *__restrict__ w, int64_t rows, int64_t k,
+                                                 const uint16_t *__restrict__ a, int64_t n,
+                                                 float *__restrict__ out, int nrt, int nct)
+{
+    constexpr int WM = BM / 2, WN = BN / 2;       // wave tile
+    constexpr int TM = WM / 32, TN = WN / 32;     // 32x32 MFMA tiles per wave
+    constexpr int AU = BM / 32;                   // activation units per thread per stage
+    constexpr int WU = BN / 32;                   // weight units per thread per stage
+    constexpr int ROWH = kFKS;                    // halves per LDS row (128 bytes)
+    constexpr int BUFH = (BM + BN) * ROWH;        // halves per LDS buffer
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUFH];
+
+    const int ntiles = nrt * nct;
+    const int b = blockIdx.x;
+    const int xcd = b & 7, pos = b >> 3, q = ntiles >> 3, rem = ntiles & 7;
+    const int t = xcd * q + (xcd < rem ? xcd : rem) + pos;
+    const int64_t r0 = (int64_t)(t / nct) * BN;
+    const int64_t c0 = (int64_t)(t % nct) * BM;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 31;
+    const int hi = lane >> 5;
+
+    // Tile resources (bytes of the valid rows of this tile).
+    const int64_t arows = n - c0 < BM ? n - c0 : BM;
+    const int64_t wrows = rows - r0 < BN ? rows - r0 : BN;
+    const __amdgpu_buffer_rsrc_t ar = tile_rsrc(a + c0 * k, arows * k * 2);
+    const __amdgpu_buffer_rsrc_t wr = tile_rsrc(w + r0 * k, wrows * k * 2);
+    // This thread's units: rows (tid >> 3) + 32 p, 16-byte chunk tid & 7.  All
+    // of a load's offset is in the VGPR offset, which the buffer range check
+    // covers; an offset at or past the resource size reads as zero.
+    const int urow = tid >> 3, uch = tid & 7;
+    const int voff = (int)(urow * k * 2 + uch * 16);
+    const int rstride = (int)(32 * k * 2);          // bytes between p and p + 1
+    const int past_end = 256 * (int)k * 2;          // >= every tile's resource size
+    const int64_t nstages = k / kFKS;
+    // LDS byte offsets of this thread's unit stores (row urow + 32 p, swizzled chunk)
+    const int st_off = urow * (ROWH * 2) + 16 * (uch ^ ((urow >> 1) & 7));
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+
+    u32x4 areg[2][AU], wreg[2][WU];
+    auto fetch = [&](int64_t s, int set) {
+        const bool live = s < nstages;
+        const int so = (int)(s * kFKS * 2);
+#pragma unroll
+        for (int p = 0; p < AU; p++)
+            areg[set][p] = __builtin_amdgcn_raw_buffer_load_b128(ar, live ? voff + p * rstride + so : past_end, 0, 0);
+#pragma unroll
+        for (int p = 0; p < WU; p++)
+            wreg[set][p] = __builtin_amdgcn_raw_buffer_load_b128(wr, live ? voff + p * rstride + so : past_end, 0, 0);
+    };
+    auto stash = [&](int set, int buf) {
+        unsigned char *base = reinterpret_cast<unsigned char *>(smem + buf * BUFH);
+#pragma unroll
+        for (int p = 0; p < AU; p++)
+            *reinterpret_cast<u32x4 *>(base + st_off + p * 32 * ROWH * 2) = areg[set][p];
+#pragma unroll
+        for (int p = 0; p < WU; p++)
+            *reinterpret_cast<u32x4 *>(base + BM * ROWH * 2 + st_off + p * 32 * ROWH * 2) = wreg[set][p];
+    };
+    // Fragment rows of this lane: wm*WM + i*32 + lr (activations) and
+    // wn*WN + j*32 + lr (weights); all are lr modulo 16, so the swizzle is
+    // the same (lr >> 1) & 7 for every fragment.
+    const int sw = (lr >> 1) & 7;
+    auto compute = [&](int buf) {
+        const unsigned char *base = reinterpret_cast<const unsigned char *>(smem + buf * BUFH);
+        const unsigned char *abase = base + (wm * WM + lr) * (ROWH * 2);
+        const unsigned char *wbase = base + BM * ROWH * 2 + (wn * WN + lr) * (ROWH * 2);
+#pragma unroll
+        for (int kk = 0; kk < kFKS / 16; kk++) {
+            const int ch = 16 * ((2 * kk + hi) ^ sw);
+            // let the scheduler interleave the fragment reads with the MFMAs
+            __builtin_amdgcn_iglp_opt(0);
+            half8 af[TM], bf[TN];
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+                af[i] = *reinterpret_cast<const half8 *>(abase + i * 32 * ROWH * 2 + ch);
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+                bf[j] = *reinterpret_cast<const half8 *>(wbase + j * 32 * ROWH * 2 + ch);
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // Stage s waits in register set s % 2 and is computed from LDS buffer s % 2.
+    fetch(0, 0);
+    fetch(1, 1);
+    stash(0, 0);
+    __syncthreads();
+    for (int64_t s = 0; s < nstages; s += 2) {
+        fetch(s + 2, 0);
+        compute(0);
+        stash(1, 1);
+        __syncthreads();
+        fetch(s + 3, 1);
+        compute(1);
+        stash(0, 0);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int64_t r = r0 + wn * WN + j * 32 + lr;
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int64_t c = c0 + wm * WM + i * 32 + 8 * (v / 4) + 4 * hi + (v % 4);
+                if (r < rows && c < n) out[c * rows + r] = acc[i][j][v];
+            }
+        }
+}
+
 template <int BM, int BN>
 hipError_t launch_tiles(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
                         float *out, hipStream_t stream)
@@ -181,7 +326,7 @@ hipError_t launch_tiles(const uint16_t *w, int64_t rows, int64_t k, const uint16
     const int64_t nrt = (rows + BN - 1) / BN;
     const int64_t nct = (n + BM - 1) / BM;
     if (nrt * nct > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
-    mfma_kernel<BM, BN><<<dim3((uint32_t)(nrt * nct)), dim3(256), 0, stream>>>(w, rows, k, a, n, out,
+    mfma_generic<BM, BN><<<dim3((uint32_t)(nrt * nct)), dim3(256), 0, stream>>>(w, rows, k, a, n, out,
                                                                            (int)nrt, (int)nct);
     return hipGetLastError();
 }
@@ -192,9 +337,22 @@ hipError_t launch_mfma(const uint16_t *w, int64_t rows, int64_t k, const uint16_
                        float *out, hipStream_t stream)
 {
     // 256 x 256 tiles when they still give at least one block per CU,
-    // 128 x 128 otherwise.
+    // 128 x 128 otherwise.  The fast kernel needs k % 64 == 0 and 32-bit
+    // byte offsets inside one 256-row tile.
     const int64_t big = ((rows + 255) / 256) * ((n + 255) / 256);
-    if (big >= 256) return launch_tiles<256, 256>(w, rows, k, a, n, out, stream);
+    const bool fast = k % kFKS == 0 && k > 0 && 256 * k * 2 < ((int64_t)1 << 31);
+    if (fast) {
+        const bool use_big = big >= 256;
+        const int B = use_big ? 256 : 128;
+        const int64_t nrt = (rows + B - 1) / B, nct = (n + B - 1) / B;
+        if (nrt * nct > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
+        const dim3 grid((uint32_t)(nrt * nct));
+        if (use_big)
+            mfma_fast<256, 256><<<grid, dim3(256), 0, stream>>>(w, rows, k, a, n, out, (int)nrt, (int)nct);
+        else
+            mfma_fast<128, 128><<<grid, dim3(256), 0, stream>>>(w, rows, k, a, n, out, (int)nrt, (int)nct);
+        return hipGetLastError();
+    }
     return launch_tiles<128, 128>(w, rows, k, a, n, out, stream);
 }
 
