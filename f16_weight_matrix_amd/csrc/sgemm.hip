@@ -64,21 +64,30 @@ __device__ __forceinline__ void fetch_stage(u32x4 (&wreg)[2], u32x4 (&areg)[2], 
     }
 }
 
-// One step t (8 elements) for the thread's 4 x 4 elements x 8 chain lanes.
-__device__ __forceinline__ void chain_step(float (&acc)[4][4][8], const u32x4 (*Ws)[kBM],
-                                           const u32x4 (*As)[kBN], int s, int tx, int ty)
+// Operands of one step t (8 elements): the thread's 4 weight vectors and 4
+// activation vectors.
+struct StepRegs {
+    u32x4 w[4], a[4];
+};
+
+__device__ __forceinline__ void read_step(StepRegs &r, const u32x4 (*Ws)[kBM], const u32x4 (*As)[kBN],
+                                          int s, int tx, int ty)
 {
-    u32x4 wv[4], av[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) wv[i] = Ws[s][tx + 16 * i];
+    for (int i = 0; i < 4; i++) r.w[i] = Ws[s][tx + 16 * i];
 #pragma unroll
-    for (int j = 0; j < 4; j++) av[j] = As[s][ty + 16 * j];
+    for (int j = 0; j < 4; j++) r.a[j] = As[s][ty + 16 * j];
+}
+
+// One chain step for the thread's 4 x 4 elements x 8 chain lanes.
+__device__ __forceinline__ void chain_step(float (&acc)[4][4][8], const StepRegs &r)
+{
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const half8 wh = __builtin_bit_cast(half8, wv[i]);
+        const half8 wh = __builtin_bit_cast(half8, r.w[i]);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const half8 ah = __builtin_bit_cast(half8, av[j]);
+            const half8 ah = __builtin_bit_cast(half8, r.a[j]);
 #pragma unroll
             for (int l = 0; l < 8; l++)
                 acc[i][j][l] = __builtin_fmaf((float)wh[l], (float)ah[l], acc[i][j][l]);
@@ -124,10 +133,22 @@ __global__ __launch_bounds__(256) void sgemm_kernel(const uint16_t *__restrict__
             fetch_stage<kAligned>(wreg, areg, w, rows, k, a, n, row0, col0, kv0 + kBKV, kvs, tid);
         const int64_t left = kvs - kv0;
         if (left >= kBKV) {
-#pragma unroll 2
-            for (int s = 0; s < kBKV; s++) chain_step(acc, Ws, As, s, tx, ty);
+            // operands of step s + 1 are read from LDS while step s computes
+            StepRegs r0, r1;
+            read_step(r0, Ws, As, 0, tx, ty);
+#pragma unroll
+            for (int s2 = 0; s2 < kBKV; s2 += 2) {
+                read_step(r1, Ws, As, s2 + 1, tx, ty);
+                chain_step(acc, r0);
+                if (s2 + 2 < kBKV) read_step(r0, Ws, As, s2 + 2, tx, ty);
+                chain_step(acc, r1);
+            }
         } else {
-            for (int s = 0; s < (int)left; s++) chain_step(acc, Ws, As, s, tx, ty);
+            for (int s2 = 0; s2 < (int)left; s2++) {
+                StepRegs r;
+                read_step(r, Ws, As, s2, tx, ty);
+                chain_step(acc, r);
+            }
         }
     }
 
