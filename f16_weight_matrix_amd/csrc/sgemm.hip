@@ -6,19 +6,31 @@
 // ascending t, each step an FMA; the element is then reduced
 // ((l0 + l4) + (l2 + l6)) + ((l1 + l5) + (l3 + l7)).  Register blocking decides
 // who computes an element, never its bits.  Matrix products (mat_mul_par):
-// out[c*rows + r].
+// out[c*rows + r]; the activation columns are widened once per product.
 //
-// gfx950 design: VALU fp32 FMAs (the order forbids the matrix cores).  A
-// 256-thread block owns a 64-row x 64-column tile of outputs; each thread owns
-// 4 rows x 4 columns x all 8 chain lanes = 128 accumulators, so the final
-// reduction is in-register.  Per step t of 8 elements a thread reads four
-// 16-byte weight vectors and four 16-byte activation vectors from LDS and
-// issues 128 FMAs whose f16 operands are widened exactly by v_fma_mix_f32.
-// Tiles are staged global -> registers -> LDS, with the next stage's global
-// loads in flight while the current stage computes.
+// gfx950 design (VALU fp32 FMAs; the order rules out the matrix cores):
+//  - The eight chain lanes of an element are split over four threads: thread
+//    q of an element group owns lanes q and q + 4.  The hsum then starts
+//    in-thread ((l_q + l_{q+4})) and finishes with a shuffle between q and
+//    q ^ 2 ((l0+l4) + (l2+l6) and (l1+l5) + (l3+l7)) and one between q and
+//    q ^ 1: the page's tree exactly.
+//  - A 256-thread block owns a 64-row x 64-column output tile; each thread
+//    owns 8 rows x 8 columns x its 2 lanes = 128 accumulators.
+//  - Each 64-element k stage is loaded from global memory as f16, widened
+//    exactly to f32 once and stored in LDS as, for every lane pair q and
+//    every pair of steps, the four values (x[8t+q], x[8t+q+4], x[8t+8+q],
+//    x[8t+8+q+4]): one 16-byte LDS read feeds 16 FMAs of a thread (two
+//    steps of both its lanes for one row or column).  The FMAs are plain
+//    v_fma_f32 (full rate; the f16-operand form runs at two thirds of it).
+//  - Stages past k are zero (loads beyond the row read nothing): a chain
+//    step adding fma(0, 0, acc) = acc + 0 leaves every accumulator
+//    unchanged, because an accumulator that starts at +0 never becomes -0.
+//  - Blocks walk the output tiles in an XCD-aware order (block b runs on
+//    XCD b % 8, each XCD takes a contiguous range of tiles, the column tiles
+//    of one weight-row block are consecutive), so each weight row block is
+//    read from HBM once and re-read from that XCD's L2.
 //
-// ALU-bound: rows*n*k FMAs; each weight byte is re-read n/64 times and each
-// activation byte rows/64 times, from L2.
+// ALU-bound: rows*n*k FMAs.
 #include "kernels.h"
 
 namespace f16wm {
@@ -26,10 +38,15 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 64;    // weight rows per block
-constexpr int kBN = 64;    // activation columns per block
-constexpr int kBKV = 8;    // 8-element k vectors per stage (64 elements)
+constexpr int kBM = 64;              // weight rows per block
+constexpr int kBN = 64;              // activation columns per block
+constexpr int kKS = 64;              // k per stage: 8 chain steps
+constexpr int kTP = kKS / 16;        // step pairs per stage
+constexpr int kQS = kTP * 64 + 4;    // f32x4 slots between lane-pair groups (4 KB + 64 B)
+constexpr int kOp = 4 * kQS;         // f32x4 slots of one operand per buffer
 
 template <bool kAligned>
 __device__ __forceinline__ u32x4 load8(const uint16_t *p)
@@ -43,124 +60,129 @@ __device__ __forceinline__ u32x4 load8(const uint16_t *p)
     return v;
 }
 
-// Global -> registers for one stage: 2 weight and 2 activation vectors.
+// Global -> registers for one stage: 2 weight and 2 activation 8-element units
+// per thread (unit idx: row idx >> 3, step idx & 7), zero past rows, n or k.
 template <bool kAligned>
 __device__ __forceinline__ void fetch_stage(u32x4 (&wreg)[2], u32x4 (&areg)[2], const uint16_t *w,
                                             int64_t rows, int64_t k, const uint16_t *a, int64_t n,
-                                            int64_t row0, int64_t col0, int64_t kv0, int64_t kvs,
-                                            int tid)
+                                            int64_t row0, int64_t col0, int64_t k0, int tid)
 {
 #pragma unroll
     for (int p = 0; p < 2; p++) {
-        const int idx = tid + 256 * p;
-        const int rr = idx >> 3, kk = idx & 7;
-        const int64_t gk = kv0 + kk;
+        const int idx = p * 256 + tid;
+        const int rr = idx >> 3;
+        const int64_t gk = k0 + 8 * (idx & 7);
         const int64_t gr = row0 + rr, gc = col0 + rr;
         u32x4 wv = {0u, 0u, 0u, 0u}, av = {0u, 0u, 0u, 0u};
-        if (gr < rows && gk < kvs) wv = load8<kAligned>(w + gr * k + gk * 8);
-        if (gc < n && gk < kvs) av = load8<kAligned>(a + gc * k + gk * 8);
+        if (gr < rows && gk < k) wv = load8<kAligned>(w + gr * k + gk);
+        if (gc < n && gk < k) av = load8<kAligned>(a + gc * k + gk);
         wreg[p] = wv;
         areg[p] = av;
     }
 }
 
-// Operands of one step t (8 elements): the thread's 4 weight vectors and 4
-// activation vectors.
-struct StepRegs {
-    u32x4 w[4], a[4];
-};
-
-__device__ __forceinline__ void read_step(StepRegs &r, const u32x4 (*Ws)[kBM], const u32x4 (*As)[kBN],
-                                          int s, int tx, int ty)
+// Widen one 8-element unit (row r, step t of the stage) and store its four
+// lane pairs: pair q goes to slot [q][t / 2][r], half (t % 2).
+__device__ __forceinline__ void stash_unit(f32x4 *op, u32x4 v, int r, int t)
 {
+    const half8 h = __builtin_bit_cast(half8, v);
+    float *base = reinterpret_cast<float *>(op + (t >> 1) * 64 + r) + 2 * (t & 1);
 #pragma unroll
-    for (int i = 0; i < 4; i++) r.w[i] = Ws[s][tx + 16 * i];
-#pragma unroll
-    for (int j = 0; j < 4; j++) r.a[j] = As[s][ty + 16 * j];
-}
-
-// One chain step for the thread's 4 x 4 elements x 8 chain lanes.
-__device__ __forceinline__ void chain_step(float (&acc)[4][4][8], const StepRegs &r)
-{
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const half8 wh = __builtin_bit_cast(half8, r.w[i]);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const half8 ah = __builtin_bit_cast(half8, r.a[j]);
-#pragma unroll
-            for (int l = 0; l < 8; l++)
-                acc[i][j][l] = __builtin_fmaf((float)wh[l], (float)ah[l], acc[i][j][l]);
-        }
+    for (int q = 0; q < 4; q++) {
+        f32x2 pr;
+        pr.x = (float)h[q];
+        pr.y = (float)h[q + 4];
+        *reinterpret_cast<f32x2 *>(base + q * kQS * 4) = pr;
     }
 }
 
 template <bool kAligned>
 __global__ __launch_bounds__(256) void sgemm_kernel(const uint16_t *__restrict__ w, int64_t rows,
                                                     int64_t k, const uint16_t *__restrict__ a,
-                                                    int64_t n, float *__restrict__ out)
+                                                    int64_t n, float *__restrict__ out, int nrt,
+                                                    int nct)
 {
-    __shared__ u32x4 Ws[kBKV][kBM];
-    __shared__ u32x4 As[kBKV][kBN];
+    __shared__ f32x4 lds[2][2 * kOp];    // [buffer][weights | activations]
+
+    // XCD-aware tile index
+    const int ntiles = nrt * nct;
+    const int b = blockIdx.x;
+    const int xcd = b & 7, pos = b >> 3, qq = ntiles >> 3, rem = ntiles & 7;
+    const int tile = xcd * qq + (xcd < rem ? xcd : rem) + pos;
+    const int64_t row0 = (int64_t)(tile / nct) * kBM;
+    const int64_t col0 = (int64_t)(tile % nct) * kBN;
 
     const int tid = threadIdx.x;
-    const int tx = tid & 15;          // rows tx + 16 i
-    const int ty = tid >> 4;          // columns ty + 16 j
-    const int64_t row0 = (int64_t)blockIdx.x * kBM;
-    const int64_t col0 = (int64_t)blockIdx.y * kBN;
-    const int64_t kvs = k >> 3;       // 8-element vectors per row
+    const int lane = tid & 63, wave = tid >> 6;
+    const int q = lane & 3;                         // lanes q and q + 4 of every element
+    const int o = lane >> 2;                        // element group within the wave (4 x 4)
+    const int orow = (wave >> 1) * 4 + (o >> 2);    // rows orow + 8 i
+    const int ocol = (wave & 1) * 4 + (o & 3);      // columns ocol + 8 j
 
-    float acc[4][4][8];
+    float acc[8][8][2];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 8; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-#pragma unroll
-            for (int l = 0; l < 8; l++) acc[i][j][l] = 0.f;
+        for (int j = 0; j < 8; j++) acc[i][j][0] = acc[i][j][1] = 0.f;
 
+    const int64_t nstages = (k + kKS - 1) / kKS;
     u32x4 wreg[2], areg[2];
-    if (kvs > 0) fetch_stage<kAligned>(wreg, areg, w, rows, k, a, n, row0, col0, 0, kvs, tid);
-    for (int64_t kv0 = 0; kv0 < kvs; kv0 += kBKV) {
-        __syncthreads();   // every thread is done reading the previous stage
+    if (nstages > 0) fetch_stage<kAligned>(wreg, areg, w, rows, k, a, n, row0, col0, 0, tid);
+    for (int64_t s = 0; s < nstages; s++) {
+        const int buf = (int)(s & 1);
+        f32x4 *wl = lds[buf];
+        f32x4 *al = lds[buf] + kOp;
+        // Buffer buf was last read two stages ago; the barrier of the previous
+        // stage separates those reads from these writes.
 #pragma unroll
         for (int p = 0; p < 2; p++) {
-            const int idx = tid + 256 * p;
-            Ws[idx & 7][idx >> 3] = wreg[p];
-            As[idx & 7][idx >> 3] = areg[p];
+            const int idx = p * 256 + tid;
+            stash_unit(wl, wreg[p], idx >> 3, idx & 7);
+            stash_unit(al, areg[p], idx >> 3, idx & 7);
         }
         __syncthreads();
-        if (kv0 + kBKV < kvs)
-            fetch_stage<kAligned>(wreg, areg, w, rows, k, a, n, row0, col0, kv0 + kBKV, kvs, tid);
-        const int64_t left = kvs - kv0;
-        if (left >= kBKV) {
-            // operands of step s + 1 are read from LDS while step s computes
-            StepRegs r0, r1;
-            read_step(r0, Ws, As, 0, tx, ty);
+        if (s + 1 < nstages)
+            fetch_stage<kAligned>(wreg, areg, w, rows, k, a, n, row0, col0, (s + 1) * kKS, tid);
+        const f32x4 *wq = wl + q * kQS;
+        const f32x4 *aq = al + q * kQS;
 #pragma unroll
-            for (int s2 = 0; s2 < kBKV; s2 += 2) {
-                read_step(r1, Ws, As, s2 + 1, tx, ty);
-                chain_step(acc, r0);
-                if (s2 + 2 < kBKV) read_step(r0, Ws, As, s2 + 2, tx, ty);
-                chain_step(acc, r1);
-            }
-        } else {
-            for (int s2 = 0; s2 < (int)left; s2++) {
-                StepRegs r;
-                read_step(r, Ws, As, s2, tx, ty);
-                chain_step(acc, r);
-            }
+        for (int tp = 0; tp < kTP; tp++) {
+            f32x4 wv[8], av[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) wv[i] = wq[tp * 64 + orow + 8 * i];
+#pragma unroll
+            for (int j = 0; j < 8; j++) av[j] = aq[tp * 64 + ocol + 8 * j];
+            // step 2 tp, then step 2 tp + 1, for lanes q (x, z) and q + 4 (y, w)
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    acc[i][j][0] = __builtin_fmaf(wv[i].x, av[j].x, acc[i][j][0]);
+                    acc[i][j][1] = __builtin_fmaf(wv[i].y, av[j].y, acc[i][j][1]);
+                }
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    acc[i][j][0] = __builtin_fmaf(wv[i].z, av[j].z, acc[i][j][0]);
+                    acc[i][j][1] = __builtin_fmaf(wv[i].w, av[j].w, acc[i][j][1]);
+                }
         }
     }
 
+    // hsum: (l_q + l_{q+4}) in-thread, then with q ^ 2, then with q ^ 1.
+    // Every lane of the group ends with the element; lane q stores the
+    // columns j with j % 4 == q.
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int64_t r = row0 + tx + 16 * i;
+    for (int i = 0; i < 8; i++) {
+        const int64_t r = row0 + orow + 8 * i;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int64_t c = col0 + ty + 16 * j;
-            const float v = ((acc[i][j][0] + acc[i][j][4]) + (acc[i][j][2] + acc[i][j][6])) +
-                            ((acc[i][j][1] + acc[i][j][5]) + (acc[i][j][3] + acc[i][j][7]));
-            if (r < rows && c < n) out[c * rows + r] = v;
+        for (int j = 0; j < 8; j++) {
+            float v = acc[i][j][0] + acc[i][j][1];
+            v = v + __shfl_xor(v, 2);
+            v = v + __shfl_xor(v, 1);
+            const int64_t c = col0 + ocol + 8 * j;
+            if ((j & 3) == q && r < rows && c < n) out[c * rows + r] = v;
         }
     }
 }
@@ -170,22 +192,15 @@ __global__ __launch_bounds__(256) void sgemm_kernel(const uint16_t *__restrict__
 hipError_t launch_sgemm(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
                         float *out, bool aligned16, hipStream_t stream)
 {
-    const int64_t bx = (rows + kBM - 1) / kBM;
-    const int64_t by_all = (n + kBN - 1) / kBN;
-    if (bx > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
-    for (int64_t b0 = 0; b0 < by_all; b0 += 65535) {
-        const int64_t by = by_all - b0 < 65535 ? by_all - b0 : 65535;
-        const int64_t c0 = b0 * kBN;
-        const int64_t nc = n - c0 < by * kBN ? n - c0 : by * kBN;
-        const dim3 grid((uint32_t)bx, (uint32_t)by);
-        if (aligned16)
-            sgemm_kernel<true><<<grid, dim3(256), 0, stream>>>(w, rows, k, a + c0 * k, nc, out + c0 * rows);
-        else
-            sgemm_kernel<false><<<grid, dim3(256), 0, stream>>>(w, rows, k, a + c0 * k, nc, out + c0 * rows);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    const int64_t nrt = (rows + kBM - 1) / kBM;
+    const int64_t nct = (n + kBN - 1) / kBN;
+    if (nrt * nct > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
+    const dim3 grid((uint32_t)(nrt * nct));
+    if (aligned16)
+        sgemm_kernel<true><<<grid, dim3(256), 0, stream>>>(w, rows, k, a, n, out, (int)nrt, (int)nct);
+    else
+        sgemm_kernel<false><<<grid, dim3(256), 0, stream>>>(w, rows, k, a, n, out, (int)nrt, (int)nct);
+    return hipGetLastError();
 }
 
 }  // namespace f16wm
