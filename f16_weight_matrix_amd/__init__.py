@@ -55,11 +55,13 @@ def lib() -> ctypes.CDLL:
         L.f16wm_to_f16.argtypes = [P, P, I64, P]
         L.f16wm_mat_vec.argtypes = [P, I64, I64, P, P, P]
         L.f16wm_mat_vec_multi.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, P]
+        L.f16wm_mat_vec_f32.argtypes = [P, I64, I64, P, P, P]
+        L.f16wm_mat_vec_multi_f32.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, P]
         L.f16wm_mat_mul.argtypes = [P, I64, I64, P, I64, P, P]
         L.f16wm_mat_mul_mfma.argtypes = [P, I64, I64, P, I64, P, P]
         L.f16wm_takes_sgemm.argtypes = [I64, I64, I64]
-        for f in ("f16wm_to_f16", "f16wm_mat_vec", "f16wm_mat_vec_multi", "f16wm_mat_mul",
-                  "f16wm_mat_mul_mfma", "f16wm_takes_sgemm"):
+        for f in ("f16wm_to_f16", "f16wm_mat_vec", "f16wm_mat_vec_multi", "f16wm_mat_vec_f32",
+                  "f16wm_mat_vec_multi_f32", "f16wm_mat_mul", "f16wm_mat_mul_mfma", "f16wm_takes_sgemm"):
             getattr(L, f).restype = ctypes.c_int
         L.f16wm_last_error.restype = ctypes.c_char_p
         L.f16wm_last_error.argtypes = []
@@ -136,10 +138,22 @@ def _wk(w: torch.Tensor):
     return w.shape[0], w.shape[1]
 
 
+def _act(a: torch.Tensor, name: str) -> bool:
+    """Check an activation column: f16 bit patterns, or float32 (rounded to f16
+    inside the product).  Returns True for float32."""
+    if isinstance(a, torch.Tensor) and a.dtype == torch.float32:
+        _f32(a, name)
+        return True
+    _f16(a, name)
+    return False
+
+
 def mat_vec(w: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """out[r] = vec_dot(W[r], a): W [rows, k] f16, a [k] f16 -> [rows] f32."""
+    """out[r] = vec_dot(W[r], a): W [rows, k] f16, a [k] f16 -> [rows] f32.
+    A float32 `a` is rounded to f16 inside the same launch (equal to
+    to_f16(a) first, bit for bit)."""
     rows, k = _wk(w)
-    _f16(a, "a")
+    f32 = _act(a, "a")
     if a.numel() != k:
         raise ValueError("a must have k = %d elements" % k)
     if out is None:
@@ -147,13 +161,15 @@ def mat_vec(w: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = None) -
     _f32(out, "out")
     if out.numel() != rows:
         raise ValueError("out must have rows = %d elements" % rows)
+    fn = lib().f16wm_mat_vec_f32 if f32 else lib().f16wm_mat_vec
     with torch.cuda.device(w.device):
-        _check(lib().f16wm_mat_vec(w.data_ptr(), rows, k, a.data_ptr(), out.data_ptr(), _stream(w.device)))
+        _check(fn(w.data_ptr(), rows, k, a.data_ptr(), out.data_ptr(), _stream(w.device)))
     return out
 
 
 def mat_vec_multi(ws, a: torch.Tensor, outs=None) -> list:
-    """Several matrices with the same k times one f16 column, in one launch."""
+    """Several matrices with the same k times one f16 column, in one launch
+    (a float32 column is rounded to f16 inside that launch)."""
     ws = list(ws)
     if not 1 <= len(ws) <= MAX_MULTI:
         raise ValueError("1..%d matrices" % MAX_MULTI)
@@ -164,7 +180,7 @@ def mat_vec_multi(ws, a: torch.Tensor, outs=None) -> list:
             k = kk
         elif kk != k:
             raise ValueError("all matrices must share k")
-    _f16(a, "a")
+    f32 = _act(a, "a")
     if a.numel() != k:
         raise ValueError("a must have k = %d elements" % k)
     if outs is None:
@@ -181,8 +197,9 @@ def mat_vec_multi(ws, a: torch.Tensor, outs=None) -> list:
         mats[i].rows = w.shape[0]
         mats[i].out = o.data_ptr()
     dev = ws[0].device
+    fn = lib().f16wm_mat_vec_multi_f32 if f32 else lib().f16wm_mat_vec_multi
     with torch.cuda.device(dev):
-        _check(lib().f16wm_mat_vec_multi(mats, len(ws), k, a.data_ptr(), _stream(dev)))
+        _check(fn(mats, len(ws), k, a.data_ptr(), _stream(dev)))
     return outs
 
 

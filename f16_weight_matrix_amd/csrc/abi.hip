@@ -89,8 +89,10 @@ int launched(const char *fn, hipError_t e)
 
 bool aligned(const void *p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 
-// Checks common to the products: sizes, overflow, null pointers, alignment.
-int check_product(const char *fn, const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a,
+// Checks common to the products: sizes, overflow, null pointers, alignment
+// and overlap.  The activation has n*k elements of a_es bytes (2: f16 bit
+// patterns, 4: f32 values).
+int check_product(const char *fn, const uint16_t *w, int64_t rows, int64_t k, const void *a, int a_es,
                   int64_t n, const float *out, int64_t *w_elems, int64_t *a_elems, int64_t *o_elems)
 {
     if (rows < 0 || k < 0 || n < 0)
@@ -101,10 +103,10 @@ int check_product(const char *fn, const uint16_t *w, int64_t rows, int64_t k, co
                     fn, (long long)rows, (long long)k, (long long)n);
     if ((*w_elems > 0 && !w) || (*a_elems > 0 && !a) || (*o_elems > 0 && !out))
         return fail(F16WM_EINVAL, "%s: null pointer for a non-empty array", fn);
-    if (!aligned(w, 2) || !aligned(a, 2) || !aligned(out, 4))
+    if (!aligned(w, 2) || !aligned(a, (uintptr_t)a_es) || !aligned(out, 4))
         return fail(F16WM_EINVAL, "%s: misaligned pointer (f16 arrays need 2 bytes, f32 arrays 4)", fn);
     const Span so = span(out, *o_elems * 4);
-    if (overlap(so, span(w, *w_elems * 2)) || overlap(so, span(a, *a_elems * 2)))
+    if (overlap(so, span(w, *w_elems * 2)) || overlap(so, span(a, *a_elems * a_es)))
         return fail(F16WM_EINVAL, "%s: output overlaps an input", fn);
     return F16WM_OK;
 }
@@ -137,12 +139,17 @@ int f16wm_to_f16(const float *x, uint16_t *y, int64_t count, void *stream)
     return launched(fn, f16wm::launch_to_f16(x, y, count, (hipStream_t)stream));
 }
 
-int f16wm_mat_vec(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, float *out,
-                  void *stream)
+}  // extern "C"
+
+namespace {
+
+// mat_vec with an f16 (f32act = false) or f32 (rounded in the kernel)
+// activation column.
+int mat_vec_impl(const char *fn, const uint16_t *w, int64_t rows, int64_t k, const void *a, bool f32act,
+                 float *out, void *stream)
 {
-    const char *fn = "f16wm_mat_vec";
     int64_t we, ae, oe;
-    if (int rc = check_product(fn, w, rows, k, a, 1, out, &we, &ae, &oe)) return rc;
+    if (int rc = check_product(fn, w, rows, k, a, f32act ? 4 : 2, 1, out, &we, &ae, &oe)) return rc;
     if (rows == 0) return ok();
     if (int rc = check_device(fn)) return rc;
     f16wm::RowTable t = {};
@@ -152,16 +159,16 @@ int f16wm_mat_vec(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a,
     t.row0[0] = 0;
     t.row0[1] = rows;
     const bool vec8 = k % 8 == 0 && aligned(w, 16) && aligned(a, 16);
-    return launched(fn, f16wm::launch_vec_dot(t, k, a, 1, vec8, (hipStream_t)stream));
+    return launched(fn, f16wm::launch_vec_dot(t, k, a, f32act, 1, vec8, (hipStream_t)stream));
 }
 
-int f16wm_mat_vec_multi(const f16wm_mat *mats, int32_t count, int64_t k, const uint16_t *a,
-                        void *stream)
+int mat_vec_multi_impl(const char *fn, const f16wm_mat *mats, int32_t count, int64_t k, const void *a,
+                       bool f32act, void *stream)
 {
-    const char *fn = "f16wm_mat_vec_multi";
     if (count < 1 || count > F16WM_MAX_MULTI)
         return fail(F16WM_EINVAL, "%s: count %d outside 1..%d", fn, (int)count, F16WM_MAX_MULTI);
     if (!mats) return fail(F16WM_EINVAL, "%s: null descriptor array", fn);
+    if (k < 0) return fail(F16WM_EINVAL, "%s: negative size (k=%lld)", fn, (long long)k);
     f16wm::RowTable t = {};
     t.count = count;
     bool vec8 = k % 8 == 0 && aligned(a, 16);
@@ -170,7 +177,8 @@ int f16wm_mat_vec_multi(const f16wm_mat *mats, int32_t count, int64_t k, const u
         int64_t we, ae, oe;
         char name[64];
         snprintf(name, sizeof name, "%s[%d]", fn, m);
-        if (int rc = check_product(name, mats[m].w, mats[m].rows, k, a, 1, mats[m].out, &we, &ae, &oe))
+        if (int rc = check_product(name, mats[m].w, mats[m].rows, k, a, f32act ? 4 : 2, 1, mats[m].out, &we,
+                                   &ae, &oe))
             return rc;
         for (int j = 0; j < m; j++) {
             // no output may overlap another matrix or another output
@@ -191,7 +199,35 @@ int f16wm_mat_vec_multi(const f16wm_mat *mats, int32_t count, int64_t k, const u
     t.row0[count] = total;
     if (total == 0) return ok();
     if (int rc = check_device(fn)) return rc;
-    return launched(fn, f16wm::launch_vec_dot(t, k, a, 1, vec8, (hipStream_t)stream));
+    return launched(fn, f16wm::launch_vec_dot(t, k, a, f32act, 1, vec8, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int f16wm_mat_vec(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, float *out,
+                  void *stream)
+{
+    return mat_vec_impl("f16wm_mat_vec", w, rows, k, a, false, out, stream);
+}
+
+int f16wm_mat_vec_f32(const uint16_t *w, int64_t rows, int64_t k, const float *x, float *out,
+                      void *stream)
+{
+    return mat_vec_impl("f16wm_mat_vec_f32", w, rows, k, x, true, out, stream);
+}
+
+int f16wm_mat_vec_multi(const f16wm_mat *mats, int32_t count, int64_t k, const uint16_t *a,
+                        void *stream)
+{
+    return mat_vec_multi_impl("f16wm_mat_vec_multi", mats, count, k, a, false, stream);
+}
+
+int f16wm_mat_vec_multi_f32(const f16wm_mat *mats, int32_t count, int64_t k, const float *x,
+                            void *stream)
+{
+    return mat_vec_multi_impl("f16wm_mat_vec_multi_f32", mats, count, k, x, true, stream);
 }
 
 int f16wm_mat_mul(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
@@ -199,7 +235,7 @@ int f16wm_mat_mul(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a,
 {
     const char *fn = "f16wm_mat_mul";
     int64_t we, ae, oe;
-    if (int rc = check_product(fn, w, rows, k, a, n, out, &we, &ae, &oe)) return rc;
+    if (int rc = check_product(fn, w, rows, k, a, 2, n, out, &we, &ae, &oe)) return rc;
     if (rows == 0 || n == 0) return ok();
     if (int rc = check_device(fn)) return rc;
     const bool al16 = aligned(w, 16) && aligned(a, 16);
@@ -212,7 +248,7 @@ int f16wm_mat_mul(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a,
     t.row0[0] = 0;
     t.row0[1] = rows;
     const bool vec8 = k % 8 == 0 && al16;
-    return launched(fn, f16wm::launch_vec_dot(t, k, a, n, vec8, (hipStream_t)stream));
+    return launched(fn, f16wm::launch_vec_dot(t, k, a, false, n, vec8, (hipStream_t)stream));
 }
 
 int f16wm_mat_mul_mfma(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
@@ -220,7 +256,7 @@ int f16wm_mat_mul_mfma(const uint16_t *w, int64_t rows, int64_t k, const uint16_
 {
     const char *fn = "f16wm_mat_mul_mfma";
     int64_t we, ae, oe;
-    if (int rc = check_product(fn, w, rows, k, a, n, out, &we, &ae, &oe)) return rc;
+    if (int rc = check_product(fn, w, rows, k, a, 2, n, out, &we, &ae, &oe)) return rc;
     if (k % 8 != 0 || !aligned(w, 16) || !aligned(a, 16))
         return fail(F16WM_EUNSUPPORTED, "%s: needs k %% 8 == 0 and 16-byte aligned w and a (k=%lld)", fn,
                     (long long)k);

@@ -21,9 +21,11 @@ struct RowTable {
 hipError_t launch_to_f16(const float *x, uint16_t *y, int64_t count, hipStream_t stream);
 
 // vec_dot order for `ncols` activation columns (column c at a + c*k, output
-// of matrix m column c at out[m] + c*rows_m).  vec8 needs k % 8 == 0 and
-// 16-byte aligned w[] and a.
-hipError_t launch_vec_dot(const RowTable &t, int64_t k, const uint16_t *a, int64_t ncols,
+// of matrix m column c at out[m] + c*rows_m).  The activation is f16 bit
+// patterns, or f32 values (f32act) rounded in the kernel exactly as
+// launch_to_f16 rounds them.  vec8 needs k % 8 == 0 and 16-byte aligned w[]
+// and a.
+hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32act, int64_t ncols,
                           bool vec8, hipStream_t stream);
 
 // tinyBLAS order (rows % 4 == 0, k % 8 == 0, n >= 2 checked by the caller).

@@ -1,27 +1,14 @@
-// Activation rounding: binary32 -> binary16, round to nearest even.
-//
-// bankML f16 page, Design notes ("Activation"): before any product the f32
-// activation is rounded to f16 with round-to-nearest-even (F16C vcvtps2ph with
-// immediate 0).  On gfx950 v_cvt_f16_f32 rounds by the MODE register, which is
-// round-to-nearest-even for HIP kernels, keeps f16 subnormals and overflows to
-// infinity; NaNs are re-encoded explicitly as a quiet NaN with the sign and
-// the top ten payload bits (the F16C result).
+// Activation rounding: binary32 -> binary16, round to nearest even
+// (bankML f16 page, Design notes, "Activation"; the rounding itself is
+// rne_f16 in f16_round.h, shared with the fused-activation products).
 //
 // HBM-bound: 4 bytes in, 2 bytes out per element.  Each thread converts eight
 // elements with two 16-byte loads and one 16-byte store.
+#include "f16_round.h"
 #include "kernels.h"
 
 namespace f16wm {
 namespace {
-
-__device__ __forceinline__ uint16_t rne_f16(float x)
-{
-    uint32_t b = __float_as_uint(x);
-    uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)x);
-    if ((b & 0x7fffffffu) > 0x7f800000u)
-        h = (uint16_t)(((b >> 16) & 0x8000u) | 0x7e00u | ((b >> 13) & 0x3ffu));
-    return h;
-}
 
 template <bool kVec>
 __global__ __launch_bounds__(256) void to_f16_kernel(const float *__restrict__ x,

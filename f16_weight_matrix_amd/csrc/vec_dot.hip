@@ -27,6 +27,7 @@
 //
 // HBM-bound: 2*k bytes of weight per row, read once, with the activation
 // column (2*k bytes) served from cache.
+#include "f16_round.h"
 #include "kernels.h"
 
 namespace f16wm {
@@ -54,13 +55,38 @@ __device__ __forceinline__ int find_matrix(const RowTable &t, int64_t g)
     return m;
 }
 
+// Activation element i as an f16 bit pattern: stored f16, or an f32 value
+// rounded here exactly as f16wm_to_f16 rounds it.
+template <bool kF32>
+__device__ __forceinline__ uint16_t act16(const void *a, int64_t i)
+{
+    if (kF32) return rne_f16(static_cast<const float *>(a)[i]);
+    return static_cast<const uint16_t *>(a)[i];
+}
+
+// Eight consecutive activation elements (16-byte aligned) as f16 bit patterns.
+template <bool kF32>
+__device__ __forceinline__ u32x4 act8(const void *a, int64_t i)
+{
+    if (!kF32) return *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a) + i);
+    const float4 p = *reinterpret_cast<const float4 *>(static_cast<const float *>(a) + i);
+    const float4 q = *reinterpret_cast<const float4 *>(static_cast<const float *>(a) + i + 4);
+    u32x4 o;
+    o.x = (uint32_t)rne_f16(p.x) | ((uint32_t)rne_f16(p.y) << 16);
+    o.y = (uint32_t)rne_f16(p.z) | ((uint32_t)rne_f16(p.w) << 16);
+    o.z = (uint32_t)rne_f16(q.x) | ((uint32_t)rne_f16(q.y) << 16);
+    o.w = (uint32_t)rne_f16(q.z) | ((uint32_t)rne_f16(q.w) << 16);
+    return o;
+}
+
 // The k % 32 tail in binary64, ascending, onto the f32 tree result.
-__device__ __forceinline__ float add_tail(float v, const uint16_t *w, const uint16_t *a, int64_t from,
+template <bool kF32>
+__device__ __forceinline__ float add_tail(float v, const uint16_t *w, const void *a, int64_t from,
                                           int64_t k)
 {
     double d = (double)v;
     for (int64_t i = from; i < k; i++) {
-        const float p = widen(w[i]) * widen(a[i]);   // exact in f32
+        const float p = widen(w[i]) * widen(act16<kF32>(a, i));   // exact in f32
         d = d + (double)p;
     }
     return (float)d;
@@ -147,9 +173,8 @@ struct LdsCfg {
     static_assert(R * U % 256 == 0, "whole units per thread");
 };
 
-template <int LPR>
-__global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k,
-                                                   const uint16_t *__restrict__ a_all)
+template <int LPR, bool kF32>
+__global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const void *__restrict__ a_all)
 {
     typedef LdsCfg<LPR> C;
     typedef typename Halves<C::CPL>::T HT;
@@ -157,7 +182,7 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k,
 
     const int tid = threadIdx.x;
     const int64_t col = blockIdx.y;
-    const uint16_t *a = a_all + col * k;
+    const void *a = static_cast<const char *>(a_all) + col * k * (kF32 ? 4 : 2);
     const int64_t total = t.row0[t.count];
     const int64_t g0 = (int64_t)blockIdx.x * C::R;
 
@@ -174,7 +199,6 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k,
         }
     }
     const bool act_loader = tid < C::U;
-    const uint16_t *asrc = a + 8 * tid;
 
     const int64_t nsteps = k >> 5;                       // full 32-element steps
     const int64_t nstages = (k + C::SC - 1) / C::SC;
@@ -189,7 +213,7 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k,
             if (src[p] && k0 + 8 * (f % C::U) < k)
                 wreg[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src[p] + k0));
         }
-        if (act_loader && k0 + 8 * tid < k) areg = *reinterpret_cast<const u32x4 *>(asrc + k0);
+        if (act_loader && k0 + 8 * tid < k) areg = act8<kF32>(a, k0 + 8 * tid);
     };
     auto stash = [&](int buf) {
         unsigned char *base = lds + buf * C::BUFB;
@@ -238,7 +262,7 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k,
         const int m = find_matrix(t, g);
         const int64_t r = g - t.row0[m];
         const uint16_t *wrow = t.w[m] + r * k;
-        if (k & 31) v = add_tail(v, wrow, a, nsteps * 32, k);
+        if (k & 31) v = add_tail<kF32>(v, wrow, a, nsteps * 32, k);
         const int64_t rows_m = t.row0[m + 1] - t.row0[m];
         t.out[m][col * rows_m + r] = v;
     }
@@ -246,11 +270,11 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k,
 
 constexpr int kV1Rows = 8;    // rows per 256-thread block, 32 lanes per row
 
-__global__ __launch_bounds__(256) void vec_dot_v1(RowTable t, int64_t k,
-                                                  const uint16_t *__restrict__ a_all)
+template <bool kF32>
+__global__ __launch_bounds__(256) void vec_dot_v1(RowTable t, int64_t k, const void *__restrict__ a_all)
 {
     const int64_t col = blockIdx.y;
-    const uint16_t *a = a_all + col * k;
+    const void *a = static_cast<const char *>(a_all) + col * k * (kF32 ? 4 : 2);
     const int c = threadIdx.x & 31;
     const int64_t g = (int64_t)blockIdx.x * kV1Rows + (threadIdx.x >> 5);
     const bool valid = g < t.row0[t.count];
@@ -263,7 +287,7 @@ __global__ __launch_bounds__(256) void vec_dot_v1(RowTable t, int64_t k,
     if (valid) {
 #pragma unroll 8
         for (int64_t s = 0; s < nsteps; s++)
-            acc = __builtin_fmaf(widen(wrow[32 * s + c]), widen(a[32 * s + c]), acc);
+            acc = __builtin_fmaf(widen(wrow[32 * s + c]), widen(act16<kF32>(a, 32 * s + c)), acc);
     }
     acc = acc + __shfl_xor(acc, 16);   // a0 + a2, a1 + a3
     acc = acc + __shfl_xor(acc, 8);    // (a0 + a2) + (a1 + a3)
@@ -273,7 +297,7 @@ __global__ __launch_bounds__(256) void vec_dot_v1(RowTable t, int64_t k,
 
     if (valid && c == 0) {
         float v = acc;
-        if (k & 31) v = add_tail(v, wrow, a, nsteps * 32, k);
+        if (k & 31) v = add_tail<kF32>(v, wrow, a, nsteps * 32, k);
         const int64_t rows_m = t.row0[m + 1] - t.row0[m];
         t.out[m][col * rows_m + r] = v;
     }
@@ -281,8 +305,8 @@ __global__ __launch_bounds__(256) void vec_dot_v1(RowTable t, int64_t k,
 
 }  // namespace
 
-hipError_t launch_vec_dot(const RowTable &t, int64_t k, const uint16_t *a, int64_t ncols, bool vec8,
-                          hipStream_t stream)
+hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32act, int64_t ncols,
+                          bool vec8, hipStream_t stream)
 {
     const int64_t total = t.row0[t.count];
     // Lanes per row: 4 (64-row blocks) when that still gives two blocks per
@@ -303,17 +327,26 @@ hipError_t launch_vec_dot(const RowTable &t, int64_t k, const uint16_t *a, int64
         RowTable tc = t;
         for (int i = 0; i < t.count; i++) tc.out[i] = t.out[i] + c0 * (t.row0[i + 1] - t.row0[i]);
         const dim3 grid((uint32_t)bx, (uint32_t)nc);
-        const uint16_t *ac = a + c0 * k;
-        if (!vec8)
-            vec_dot_v1<<<grid, dim3(256), 0, stream>>>(tc, k, ac);
-        else if (lpr == 4)
-            vec_dot_lds<4><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
-        else if (lpr == 8)
-            vec_dot_lds<8><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
-        else if (lpr == 16)
-            vec_dot_lds<16><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
-        else
-            vec_dot_lds<32><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
+        const void *ac = static_cast<const char *>(a) + c0 * k * (f32act ? 4 : 2);
+        if (f32act) {
+            if (!vec8)
+                vec_dot_v1<true><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
+            else if (lpr == 4)
+                vec_dot_lds<4, true><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
+            else if (lpr == 16)
+                vec_dot_lds<16, true><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
+            else
+                vec_dot_lds<32, true><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
+        } else {
+            if (!vec8)
+                vec_dot_v1<false><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
+            else if (lpr == 4)
+                vec_dot_lds<4, false><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
+            else if (lpr == 16)
+                vec_dot_lds<16, false><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
+            else
+                vec_dot_lds<32, false><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

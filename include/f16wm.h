@@ -82,6 +82,23 @@ int f16wm_mat_vec_multi(const f16wm_mat *mats, int32_t count, int64_t k, const u
                         void *stream);
 
 /*
+ * f16wm_mat_vec_f32 / f16wm_mat_vec_multi_f32: the same products taking the
+ * activation column as k f32 values: each value is rounded to f16 exactly as
+ * f16wm_to_f16 rounds it (same code) inside the product's staging, so the
+ * result equals f16wm_to_f16 followed by f16wm_mat_vec / f16wm_mat_vec_multi,
+ * bit for bit, in one launch and without writing the rounded column out.
+ * f16 page, Design notes ("Activation": the activation is rounded before any
+ * product) and Matrix products; bankML page "bankML/forward.rs", Advantages
+ * and efficiency (one rounded activation feeds Q, K and V, another feeds gate
+ * and up).  x: k f32 (4-byte aligned; 16-byte alignment with k % 8 == 0
+ * selects the vectorised kernels).
+ */
+int f16wm_mat_vec_f32(const uint16_t *w, int64_t rows, int64_t k, const float *x, float *out,
+                      void *stream);
+int f16wm_mat_vec_multi_f32(const f16wm_mat *mats, int32_t count, int64_t k, const float *x,
+                            void *stream);
+
+/*
  * f16wm_mat_mul: out[c*rows + r] = dot(W[r], A[c]) for r < rows, c < n, with
  * the float order ggml picks by shape (f16 page, Matrix products mat_mul_par
  * and Design notes "sgemm_dot"): when f16wm_takes_sgemm(rows, k, n), every

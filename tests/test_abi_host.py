@@ -27,8 +27,9 @@ def L():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted([
-        "f16wm_to_f16", "f16wm_mat_vec", "f16wm_mat_vec_multi", "f16wm_mat_mul",
-        "f16wm_mat_mul_mfma", "f16wm_takes_sgemm", "f16wm_last_error", "f16wm_version"])
+        "f16wm_to_f16", "f16wm_mat_vec", "f16wm_mat_vec_multi", "f16wm_mat_vec_f32",
+        "f16wm_mat_vec_multi_f32", "f16wm_mat_mul", "f16wm_mat_mul_mfma", "f16wm_takes_sgemm",
+        "f16wm_last_error", "f16wm_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -85,6 +86,18 @@ def test_mat_vec_rejects_bad_arguments(L):
     # out (4 rows x 4 bytes) overlapping w (4 x 8 x 2 bytes)
     assert "overlap" in _err(L.f16wm_mat_vec(P, 4, 8, P + 4096, P + 16, STREAM))
     assert "overlap" in _err(L.f16wm_mat_vec(P, 4, 8, P + 4096, P + 4096, STREAM))
+
+
+def test_f32_activation_entry_points_reject_bad_arguments(L):
+    assert "null" in _err(L.f16wm_mat_vec_f32(P, 4, 8, None, P + 8192, STREAM))
+    assert "misaligned" in _err(L.f16wm_mat_vec_f32(P, 4, 8, P + 4098, P + 8192, STREAM))
+    # out (4 floats) overlapping the f32 activation (8 floats = 32 bytes)
+    assert "overlap" in _err(L.f16wm_mat_vec_f32(P, 4, 8, P + 4096, P + 4112, STREAM))
+    Mat = f16wm._Mat
+    mats = (Mat * 1)()
+    mats[0].w, mats[0].rows, mats[0].out = P, 4, P + 4120
+    assert "overlap" in _err(L.f16wm_mat_vec_multi_f32(mats, 1, 8, P + 4096, STREAM))
+    assert L.f16wm_mat_vec_f32(P, 0, 8, P + 4096, P + 8192, STREAM) == 0
 
 
 def test_mat_mul_rejects_bad_arguments(L):

@@ -44,8 +44,24 @@ def up16(x: np.ndarray, offset: int = 0) -> torch.Tensor:
     return flat.view(torch.float16).view(x.shape)
 
 
-def up32(x: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+def up32(x: np.ndarray, offset: int = 0) -> torch.Tensor:
+    flat = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32).reshape(-1)).to(DEV)
+    if offset:
+        buf = torch.empty(flat.numel() + offset, dtype=torch.float32, device=DEV)
+        buf[offset:] = flat
+        flat = buf[offset:]
+    return flat.view(x.shape)
+
+
+def f32_column(seed, k):
+    """N(0,1) f32 values with the rounding's edge cases mixed in."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(k).astype(np.float32)
+    specials = np.array([np.inf, -np.inf, np.nan, 65520.0, 65519.99, 2 ** -25, 1e-7, -0.0, 7e4,
+                         1 + 2 ** -11], dtype=np.float32)
+    idx = rng.choice(k, size=min(k // 8, specials.size), replace=False)
+    x[idx] = specials[:idx.size]
+    return x
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
@@ -230,6 +246,35 @@ def test_mat_vec_multi(orc, shapes):
     outs = f16wm.mat_vec_multi([up16(w) for w in ws], up16(a))
     for i, (w, o) in enumerate(zip(ws, outs)):
         assert_bits_equal(o.cpu().numpy(), orc.mat_vec(w, a), "multi matrix %d %s" % (i, shapes[i]))
+
+
+# ------------------------------------------- f32 activations, rounded inside
+
+@pytest.mark.parametrize("rows,k,off", [(576, 576, 0), (13, 1540, 0), (1000, 4104, 0), (100, 96, 1),
+                                        (64, 33, 3), (4096, 14336, 0), (70000, 64, 0), (5, 8, 2)])
+def test_f32_activation_equals_to_f16_then_product(orc, rows, k, off):
+    """mat_vec with an f32 column equals to_f16 then mat_vec, bit for bit
+    (edge values of the rounding included; aligned and misaligned columns)."""
+    w = synth.random_f16((71, rows, k), (rows, k), 0.02)
+    x = f32_column((72, rows, k), k)
+    want = orc.mat_vec(w, orc.to_f16(x))
+    got = f16wm.mat_vec(up16(w), up32(x, off))
+    assert_bits_equal(got.cpu().numpy(), want, "mat_vec f32 %dx%d off=%d" % (rows, k, off))
+
+
+@pytest.mark.parametrize("shapes", [
+    [(4096, 4096), (1024, 4096), (1024, 4096)],
+    [(14336, 4096), (14336, 4096)],
+    [(3, 40), (64, 40), (65, 40)],
+])
+def test_f32_activation_multi(orc, shapes):
+    k = shapes[0][1]
+    ws = [synth.random_f16((73, i, r, k), (r, k), 0.02) for i, (r, _) in enumerate(shapes)]
+    x = f32_column((74, k), k)
+    x16 = orc.to_f16(x)
+    outs = f16wm.mat_vec_multi([up16(w) for w in ws], up32(x))
+    for i, (w, o) in enumerate(zip(ws, outs)):
+        assert_bits_equal(o.cpu().numpy(), orc.mat_vec(w, x16), "multi f32 matrix %d" % i)
 
 
 # ---------------------------------------------------------- edge cases
