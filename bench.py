@@ -3,9 +3,10 @@
 
 One step is one pass of the whole hot path over one batch of synthetic input:
 
-  decode (n = 1):  to_f16 of each activation column, then
-                   Q/K/V grouped GEMV, O GEMV, gate/up grouped GEMV, down GEMV
-                   and the 128256x4096 logits GEMV (vec_dot order);
+  decode (n = 1):  Q/K/V grouped GEMV, O GEMV, gate/up grouped GEMV, down
+                   GEMV and the 128256x4096 logits GEMV (vec_dot order), each
+                   taking its f32 activation column and rounding it to f16
+                   (to_f16, same code) inside the same launch;
   prefill (n = 512): to_f16 of each 512-column activation block, then the
                    exact product of every matrix (tinyBLAS order, picked by
                    takes_sgemm) and the MFMA fp16 product of every matrix.
@@ -106,7 +107,6 @@ def main():
     dec = synth.activation(synth.CFG_8B, 0, 0, 5, 14336)
     dec_k = {"attn": 4096, "o": 4096, "ffn": 4096, "down": 14336, "logits": 4096}
     X1 = {g: torch.from_numpy(dec[i, :dec_k[g]].copy()).to(dev) for i, g in enumerate(dec_k)}
-    A1 = {g: torch.empty(dec_k[g], dtype=torch.float16, device=dev) for g in dec_k}
     # prefill activation blocks (f32) [512][k]
     pre = synth.activation(synth.CFG_8B_PREFILL, 0, 0, N, 14336)
     XN = {g: torch.from_numpy(np.ascontiguousarray(pre[:, :dec_k[g]])).to(dev) for g in dec_k}
@@ -120,19 +120,17 @@ def main():
 
     src_of = {"q": "attn", "k": "attn", "v": "attn", "o": "o", "gate": "ffn", "up": "ffn",
               "down": "down", "logits": "logits"}
-    # algorithmic bytes: weight + activation (f16) + output (f32) per GEMV
-    # launch, plus 6 bytes per activation element for its rounding (f32 read,
-    # f16 written)
+    # algorithmic bytes per GEMV launch: weights (f16) + the f32 activation
+    # column (rounded to f16 inside the launch) + outputs (f32)
     gemv_launches = [("qkv", ["q", "k", "v"], "attn"), ("o", ["o"], "o"), ("gateup", ["gate", "up"], "ffn"),
                      ("down", ["down"], "down"), ("logits", ["logits"], "logits")]
 
     def gemv_bytes(mats, g):
         k = dec_k[g]
-        return sum(2 * S[m][0] * k + 4 * S[m][0] for m in mats) + 2 * k
+        return sum(2 * S[m][0] * k + 4 * S[m][0] for m in mats) + 4 * k
 
     gemv_b = [gemv_bytes(ms, g) for _, ms, g in gemv_launches]
-    tof16_dec_bytes = sum(6 * k for k in dec_k.values())
-    decode_bytes = sum(gemv_b) + tof16_dec_bytes
+    decode_bytes = sum(gemv_b)
     flops_n512 = sum(2 * S[m][0] * S[m][1] * N for m in S)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -142,16 +140,14 @@ def main():
         ge = [(ev(), ev()) for _ in gemv_launches] if timed else None
         if timed:
             e[0].record()
-        # ---- decode, n = 1
-        for g in dec_k:
-            f16wm.to_f16(X1[g], A1[g])
+        # ---- decode, n = 1 (f32 columns, rounded to f16 inside each product)
         for i, (name, mats, g) in enumerate(gemv_launches):
             if timed:
                 ge[i][0].record()
             if len(mats) > 1:
-                f16wm.mat_vec_multi([W[m] for m in mats], A1[g], [O1[m] for m in mats])
+                f16wm.mat_vec_multi([W[m] for m in mats], X1[g], [O1[m] for m in mats])
             else:
-                f16wm.mat_vec(W[mats[0]], A1[g], O1[mats[0]])
+                f16wm.mat_vec(W[mats[0]], X1[g], O1[mats[0]])
             if timed:
                 ge[i][1].record()
         if timed:
@@ -282,7 +278,7 @@ def cpu_baseline(host_w, dec, dec_k, S, N, sample_div, gpu_value):
            "logits": "logits"}
     t = time.perf_counter()
     a16 = {g: orc.to_f16(dec[i, :dec_k[g]]) for i, g in enumerate(dec_k)}
-    nbytes = sum(6 * k + 2 * k for k in dec_k.values())   # rounding + the f16 column read
+    nbytes = sum(4 * k for k in dec_k.values())        # the f32 columns
     for m, w in host_w.items():
         k = dec_k[src[m]]
         orc.mat_vec(w, a16[src[m]], threads=T)

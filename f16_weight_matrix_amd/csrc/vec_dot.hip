@@ -173,12 +173,18 @@ struct LdsCfg {
     static_assert(R * U % 256 == 0, "whole units per thread");
 };
 
-template <int LPR, bool kF32>
+// kWhole: the whole activation column (k <= 16384 elements) is rounded or
+// copied into LDS once at the start, overlapping the first weight stage, and
+// the stages carry weights only; otherwise each stage also stages its SC
+// activation elements.  Dynamic LDS: 2 * (WBYTES, or BUFB) + (k * 2 if kWhole).
+template <int LPR, bool kF32, bool kWhole>
 __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const void *__restrict__ a_all)
 {
     typedef LdsCfg<LPR> C;
     typedef typename Halves<C::CPL>::T HT;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * C::BUFB];
+    constexpr int BUF = kWhole ? C::WBYTES : C::BUFB;   // bytes per stage buffer
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    unsigned char *actl = lds + 2 * BUF;                 // whole column (kWhole)
 
     const int tid = threadIdx.x;
     const int64_t col = blockIdx.y;
@@ -213,16 +219,16 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const 
             if (src[p] && k0 + 8 * (f % C::U) < k)
                 wreg[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src[p] + k0));
         }
-        if (act_loader && k0 + 8 * tid < k) areg = act8<kF32>(a, k0 + 8 * tid);
+        if (!kWhole && act_loader && k0 + 8 * tid < k) areg = act8<kF32>(a, k0 + 8 * tid);
     };
     auto stash = [&](int buf) {
-        unsigned char *base = lds + buf * C::BUFB;
+        unsigned char *base = lds + buf * BUF;
 #pragma unroll
         for (int p = 0; p < C::UPT; p++) {
             const int f = p * 256 + tid;
             *reinterpret_cast<u32x4 *>(base + (f / C::U) * C::ROWB + 16 * (f % C::U)) = wreg[p];
         }
-        if (act_loader) *reinterpret_cast<u32x4 *>(base + C::WBYTES + 16 * tid) = areg;
+        if (!kWhole && act_loader) *reinterpret_cast<u32x4 *>(base + C::WBYTES + 16 * tid) = areg;
     };
 
     const int rho = tid / LPR;
@@ -231,16 +237,20 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const 
 #pragma unroll
     for (int i = 0; i < C::CPL; i++) acc[i] = 0.f;
 
-    if (nstages > 0) {
-        fetch(0);
-        stash(0);
+    if (nstages > 0) fetch(0);
+    if (kWhole) {
+        // k % 8 == 0 here; visible to every thread after the barrier below
+        for (int64_t e = 8 * tid; e < k; e += 8 * 256)
+            *reinterpret_cast<u32x4 *>(actl + 2 * e) = act8<kF32>(a, e);
     }
+    if (nstages > 0) stash(0);
     __syncthreads();
     for (int64_t s = 0; s < nstages; s++) {
         const int buf = (int)(s & 1);
         if (s + 1 < nstages) fetch(s + 1);
-        const unsigned char *wl = lds + buf * C::BUFB + rho * C::ROWB + j * C::CPL * 2;
-        const unsigned char *al = lds + buf * C::BUFB + C::WBYTES + j * C::CPL * 2;
+        const unsigned char *wl = lds + buf * BUF + rho * C::ROWB + j * C::CPL * 2;
+        const unsigned char *al = kWhole ? actl + 2 * s * C::SC + j * C::CPL * 2
+                                         : lds + buf * C::BUFB + C::WBYTES + j * C::CPL * 2;
         const int64_t left = nsteps - s * (C::SC / 32);
         if (left >= C::SC / 32) {
 #pragma unroll 8
@@ -303,6 +313,45 @@ __global__ __launch_bounds__(256) void vec_dot_v1(RowTable t, int64_t k, const v
     }
 }
 
+// Whole activation column in LDS when it is at most 32 KB of f16.
+constexpr int64_t kWholeMaxK = 16384;
+
+// Allow a kernel the LDS it asks for beyond the default dynamic limit.
+template <typename K>
+void allow_lds(K kernel, size_t bytes)
+{
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int LPR>
+void launch_lds(dim3 grid, hipStream_t stream, const RowTable &t, int64_t k, const void *a, bool f32act)
+{
+    typedef LdsCfg<LPR> C;
+    static bool once = [] {
+        const size_t max_shm = 2 * C::WBYTES + (size_t)kWholeMaxK * 2;
+        allow_lds(vec_dot_lds<LPR, true, true>, max_shm);
+        allow_lds(vec_dot_lds<LPR, false, true>, max_shm);
+        allow_lds(vec_dot_lds<LPR, true, false>, 2 * C::BUFB);
+        allow_lds(vec_dot_lds<LPR, false, false>, 2 * C::BUFB);
+        return true;
+    }();
+    (void)once;
+    if (k <= kWholeMaxK) {
+        const size_t shm = 2 * C::WBYTES + (size_t)k * 2;
+        if (f32act)
+            vec_dot_lds<LPR, true, true><<<grid, dim3(256), shm, stream>>>(t, k, a);
+        else
+            vec_dot_lds<LPR, false, true><<<grid, dim3(256), shm, stream>>>(t, k, a);
+    } else {
+        const size_t shm = 2 * C::BUFB;
+        if (f32act)
+            vec_dot_lds<LPR, true, false><<<grid, dim3(256), shm, stream>>>(t, k, a);
+        else
+            vec_dot_lds<LPR, false, false><<<grid, dim3(256), shm, stream>>>(t, k, a);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32act, int64_t ncols,
@@ -328,24 +377,17 @@ hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32a
         for (int i = 0; i < t.count; i++) tc.out[i] = t.out[i] + c0 * (t.row0[i + 1] - t.row0[i]);
         const dim3 grid((uint32_t)bx, (uint32_t)nc);
         const void *ac = static_cast<const char *>(a) + c0 * k * (f32act ? 4 : 2);
-        if (f32act) {
-            if (!vec8)
+        if (!vec8) {
+            if (f32act)
                 vec_dot_v1<true><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
-            else if (lpr == 4)
-                vec_dot_lds<4, true><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
-            else if (lpr == 16)
-                vec_dot_lds<16, true><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
             else
-                vec_dot_lds<32, true><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
-        } else {
-            if (!vec8)
                 vec_dot_v1<false><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
-            else if (lpr == 4)
-                vec_dot_lds<4, false><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
-            else if (lpr == 16)
-                vec_dot_lds<16, false><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
-            else
-                vec_dot_lds<32, false><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
+        } else if (lpr == 4) {
+            launch_lds<4>(grid, stream, tc, k, ac, f32act);
+        } else if (lpr == 16) {
+            launch_lds<16>(grid, stream, tc, k, ac, f32act);
+        } else {
+            launch_lds<32>(grid, stream, tc, k, ac, f32act);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
