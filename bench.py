@@ -209,6 +209,21 @@ def main():
     rec = traffic_record(os.path.join(ROOT, "f16_weight_matrix_amd", "csrc", "vec_dot.hip"))
     traffic = rec.get("bytes_per_launch") if rec and rec.get("kernel") == "vec_dot_lds<4>" else None
 
+    # Next row beside the step: the embedding lookup of a 512-token micro-batch
+    # from the tied 128256x4096 table (get_rows), timed on its own.
+    ids = torch.from_numpy(np.random.default_rng(7).integers(0, S["logits"][0], N)).to(dev)
+    emb = torch.empty((N, S["logits"][1]), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        f16wm.get_rows(W["logits"], ids, emb)
+    ev0, ev1 = ev(), ev()
+    ev0.record()
+    for _ in range(20):
+        f16wm.get_rows(W["logits"], ids, emb)
+    ev1.record()
+    torch.cuda.synchronize()
+    gr_us = ev0.elapsed_time(ev1) * 1e3 / 20
+    gr_bytes = N * S["logits"][1] * (2 + 4) + N * 8
+
     exact_tflops = flops_n512 / (exact_avg * 1e-3) / 1e12
     mfma_tflops = flops_n512 / (mfma_avg * 1e-3) / 1e12
 
@@ -255,6 +270,8 @@ def main():
                      "achieved": round(mfma_tflops, 1), "unit": "TFLOP/s",
                      "peak": MFMA_F16_PEAK_TFLOPS, "frac": round(mfma_tflops / MFMA_F16_PEAK_TFLOPS, 4)},
         },
+        "next_rows": {"get_rows_512x4096": {"avg_us": round(gr_us, 2), "bytes": gr_bytes,
+                                            "GB_s": round(gr_bytes / (gr_us * 1e-6) / 1e9, 1)}},
         "setup_s": round(setup_s, 1),
     }
 

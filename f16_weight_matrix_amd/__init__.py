@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
         L.f16wm_to_f16.argtypes = [P, P, I64, P]
+        L.f16wm_widen.argtypes = [P, P, I64, P]
+        L.f16wm_get_rows.argtypes = [P, I64, I64, P, I64, P, P]
         L.f16wm_mat_vec.argtypes = [P, I64, I64, P, P, P]
         L.f16wm_mat_vec_multi.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, P]
         L.f16wm_mat_vec_f32.argtypes = [P, I64, I64, P, P, P]
@@ -60,7 +62,7 @@ def lib() -> ctypes.CDLL:
         L.f16wm_mat_mul.argtypes = [P, I64, I64, P, I64, P, P]
         L.f16wm_mat_mul_mfma.argtypes = [P, I64, I64, P, I64, P, P]
         L.f16wm_takes_sgemm.argtypes = [I64, I64, I64]
-        for f in ("f16wm_to_f16", "f16wm_mat_vec", "f16wm_mat_vec_multi", "f16wm_mat_vec_f32",
+        for f in ("f16wm_to_f16", "f16wm_widen", "f16wm_get_rows", "f16wm_mat_vec", "f16wm_mat_vec_multi", "f16wm_mat_vec_f32",
                   "f16wm_mat_vec_multi_f32", "f16wm_mat_mul", "f16wm_mat_mul_mfma", "f16wm_takes_sgemm"):
             getattr(L, f).restype = ctypes.c_int
         L.f16wm_last_error.restype = ctypes.c_char_p
@@ -128,6 +130,38 @@ def to_f16(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
         raise ValueError("out must match x in size and device")
     with torch.cuda.device(x.device):
         _check(lib().f16wm_to_f16(x.data_ptr(), out.data_ptr(), x.numel(), _stream(x.device)))
+    return out
+
+
+def widen(h: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Exact f16 -> f32 (same shape)."""
+    _f16(h, "h")
+    if out is None:
+        out = torch.empty(h.shape, dtype=torch.float32, device=h.device)
+    _f32(out, "out")
+    if out.numel() != h.numel() or out.device != h.device:
+        raise ValueError("out must match h in size and device")
+    with torch.cuda.device(h.device):
+        _check(lib().f16wm_widen(h.data_ptr(), out.data_ptr(), h.numel(), _stream(h.device)))
+    return out
+
+
+def get_rows(w: torch.Tensor, ids: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rows ids of W [rows, k] widened to f32: [len(ids), k] (ids int64 on the
+    GPU; an id outside [0, rows) gives a row of NaN)."""
+    rows, k = _wk(w)
+    if not isinstance(ids, torch.Tensor) or ids.dtype != torch.int64 or not ids.is_cuda \
+            or not ids.is_contiguous():
+        raise TypeError("ids must be a contiguous int64 GPU tensor")
+    n = ids.numel()
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=w.device)
+    _f32(out, "out")
+    if out.numel() != n * k:
+        raise ValueError("out must have len(ids)*k elements")
+    with torch.cuda.device(w.device):
+        _check(lib().f16wm_get_rows(w.data_ptr(), rows, k, ids.data_ptr(), n, out.data_ptr(),
+                                    _stream(w.device)))
     return out
 
 

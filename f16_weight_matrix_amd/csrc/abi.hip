@@ -206,6 +206,42 @@ int mat_vec_multi_impl(const char *fn, const f16wm_mat *mats, int32_t count, int
 
 extern "C" {
 
+int f16wm_widen(const uint16_t *h, float *y, int64_t count, void *stream)
+{
+    const char *fn = "f16wm_widen";
+    if (count < 0 || count > kMaxElems)
+        return fail(F16WM_EINVAL, "%s: bad count %lld", fn, (long long)count);
+    if (count == 0) return ok();
+    if (!h || !y) return fail(F16WM_EINVAL, "%s: null pointer", fn);
+    if (!aligned(h, 2) || !aligned(y, 4)) return fail(F16WM_EINVAL, "%s: misaligned pointer", fn);
+    if (overlap(span(h, count * 2), span(y, count * 4)))
+        return fail(F16WM_EINVAL, "%s: output overlaps the input", fn);
+    if (int rc = check_device(fn)) return rc;
+    return launched(fn, f16wm::launch_widen(h, y, count, (hipStream_t)stream));
+}
+
+int f16wm_get_rows(const uint16_t *w, int64_t rows, int64_t k, const int64_t *ids, int64_t nids,
+                   float *out, void *stream)
+{
+    const char *fn = "f16wm_get_rows";
+    int64_t we, oe;
+    if (rows < 0 || k < 0 || nids < 0)
+        return fail(F16WM_EINVAL, "%s: negative size (rows=%lld k=%lld nids=%lld)", fn, (long long)rows,
+                    (long long)k, (long long)nids);
+    if (!mul_ok(rows, k, &we) || !mul_ok(nids, k, &oe))
+        return fail(F16WM_EINVAL, "%s: size too large", fn);
+    if ((we > 0 && !w) || (nids > 0 && !ids) || (oe > 0 && !out))
+        return fail(F16WM_EINVAL, "%s: null pointer for a non-empty array", fn);
+    if (!aligned(w, 2) || !aligned(ids, 8) || !aligned(out, 4))
+        return fail(F16WM_EINVAL, "%s: misaligned pointer", fn);
+    const Span so = span(out, oe * 4);
+    if (overlap(so, span(w, we * 2)) || overlap(so, span(ids, nids * 8)))
+        return fail(F16WM_EINVAL, "%s: output overlaps an input", fn);
+    if (nids == 0 || k == 0) return ok();
+    if (int rc = check_device(fn)) return rc;
+    return launched(fn, f16wm::launch_get_rows(w, rows, k, ids, nids, out, (hipStream_t)stream));
+}
+
 int f16wm_mat_vec(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, float *out,
                   void *stream)
 {

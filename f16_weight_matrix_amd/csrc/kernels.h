@@ -33,6 +33,12 @@ hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32a
 hipError_t launch_sgemm(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
                         float *out, bool aligned16, hipStream_t stream);
 
+// Exact f16 -> f32 of count values, and of rows ids[0..nids) of W (rows x k)
+// into out[nids][k] (an id outside [0, rows) gives a row of NaN).
+hipError_t launch_widen(const uint16_t *h, float *y, int64_t count, hipStream_t stream);
+hipError_t launch_get_rows(const uint16_t *w, int64_t rows, int64_t k, const int64_t *ids, int64_t nids,
+                           float *out, hipStream_t stream);
+
 // fp16 MFMA product (k % 8 == 0, w and a 16-byte aligned).
 hipError_t launch_mfma(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
                        float *out, hipStream_t stream);

@@ -59,6 +59,25 @@ typedef struct {
 int f16wm_to_f16(const float *x, uint16_t *y, int64_t count, void *stream);
 
 /*
+ * f16wm_widen: y[i] = f32(h[i]), exact (every f16, subnormals included, is an
+ * f32; NaN stays NaN).  f16 page, Technical usage (`widen`).  h: count f16,
+ * y: count f32.
+ */
+int f16wm_widen(const uint16_t *h, float *y, int64_t count, void *stream);
+
+/*
+ * f16wm_get_rows: out[i][j] = f32(W[ids[i]][j]) for i < nids, j < k: F16
+ * weight rows widened to f32, ggml's get_rows (f16 page, Technical usage
+ * `dequantize_row`; the embedding lookup, which reads the tied token_embd
+ * matrix, bankML page "bankML/forward.rs", Summary).  w: rows x k f16; ids:
+ * nids int64 row indices in DEVICE memory; out: nids x k f32.  The ids are
+ * not visible to the host: an id outside [0, rows) is not an error, its
+ * output row is filled with quiet NaN.
+ */
+int f16wm_get_rows(const uint16_t *w, int64_t rows, int64_t k, const int64_t *ids, int64_t nids,
+                   float *out, void *stream);
+
+/*
  * f16wm_mat_vec: out[r] = vec_dot(W[r], a) for r < rows.
  * f16 page, Matrix products (mat_vec_par) and Design notes ("vec_dot"): each
  * row is four 8-lane f32 FMA accumulators over 32-element steps (accumulator
@@ -66,6 +85,8 @@ int f16wm_to_f16(const float *x, uint16_t *y, int64_t count, void *stream);
  * lanes + high four, then two horizontal adds of adjacent pairs; the k % 32
  * tail is added to that f32 in binary64, ascending, and the sum is rounded to
  * f32.  w: rows x k f16, a: k f16, out: rows f32.  k = 0 writes +0.0.
+ * The page's vec_dot_u16 (the same order with the first operand given as
+ * f16 values, e.g. K-cache rows) is this call: W is f16 values here too.
  */
 int f16wm_mat_vec(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, float *out,
                   void *stream);

@@ -27,9 +27,9 @@ def L():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted([
-        "f16wm_to_f16", "f16wm_mat_vec", "f16wm_mat_vec_multi", "f16wm_mat_vec_f32",
-        "f16wm_mat_vec_multi_f32", "f16wm_mat_mul", "f16wm_mat_mul_mfma", "f16wm_takes_sgemm",
-        "f16wm_last_error", "f16wm_version"])
+        "f16wm_to_f16", "f16wm_widen", "f16wm_get_rows", "f16wm_mat_vec", "f16wm_mat_vec_multi",
+        "f16wm_mat_vec_f32", "f16wm_mat_vec_multi_f32", "f16wm_mat_mul", "f16wm_mat_mul_mfma",
+        "f16wm_takes_sgemm", "f16wm_last_error", "f16wm_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -98,6 +98,17 @@ def test_f32_activation_entry_points_reject_bad_arguments(L):
     mats[0].w, mats[0].rows, mats[0].out = P, 4, P + 4120
     assert "overlap" in _err(L.f16wm_mat_vec_multi_f32(mats, 1, 8, P + 4096, STREAM))
     assert L.f16wm_mat_vec_f32(P, 0, 8, P + 4096, P + 8192, STREAM) == 0
+
+
+def test_widen_and_get_rows_reject_bad_arguments(L):
+    assert "bad count" in _err(L.f16wm_widen(P, P + 4096, -1, STREAM))
+    assert "misaligned" in _err(L.f16wm_widen(P, P + 4098, 4, STREAM))
+    assert "overlap" in _err(L.f16wm_widen(P, P + 4, 4, STREAM))
+    assert "negative" in _err(L.f16wm_get_rows(P, 4, 8, P + 4096, -1, P + 8192, STREAM))
+    assert "null" in _err(L.f16wm_get_rows(P, 4, 8, None, 2, P + 8192, STREAM))
+    assert "misaligned" in _err(L.f16wm_get_rows(P, 4, 8, P + 4100, 2, P + 8192, STREAM))
+    assert "overlap" in _err(L.f16wm_get_rows(P, 4, 8, P + 4096, 2, P + 4100, STREAM))
+    assert L.f16wm_get_rows(P, 4, 8, P + 4096, 0, P + 8192, STREAM) == 0
 
 
 def test_mat_mul_rejects_bad_arguments(L):

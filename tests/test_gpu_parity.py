@@ -165,6 +165,31 @@ def test_every_f16_value_widens_exactly(orc):
         assert_bits_equal(got, orc.mat_vec(w, col), "widen via vec_dot GEMV at %d" % c0)
 
 
+def test_widen_entry_point_all_patterns(orc):
+    """f16wm_widen on all 2^16 patterns (aligned and not), against the oracle."""
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    want = orc.widen(pats)
+    for off in (0, 1, 5):
+        got = f16wm.widen(up16(pats, off)).cpu().numpy()
+        assert_bits_equal(got, want, "widen offset %d" % off)
+
+
+@pytest.mark.parametrize("rows,k", [(49152, 576), (128256, 4096), (13, 31), (100, 1000)])
+def test_get_rows(orc, rows, k):
+    """Embedding lookup (get_rows / dequantize_row): selected rows widened
+    exactly; first, last and repeated ids; an out-of-range id gives NaN."""
+    w = synth.random_f16((81, rows, k), (rows, k), 0.02) if rows * k < 10 ** 8 else \
+        synth.weight(synth.CFG_8B, 0, "logits", rows, k)
+    rng = np.random.default_rng(82)
+    ids = np.concatenate([[0, rows - 1, 0], rng.integers(0, rows, 509)]).astype(np.int64)
+    got = f16wm.get_rows(up16(w), torch.from_numpy(ids).to(DEV)).cpu().numpy()
+    assert_bits_equal(got, orc.widen(w[ids]), "get_rows %dx%d" % (rows, k))
+    bad = torch.tensor([rows, -1, 2 if rows > 2 else 0], dtype=torch.int64, device=DEV)
+    g2 = f16wm.get_rows(up16(w), bad).cpu().numpy()
+    assert np.isnan(g2[:2]).all()
+    assert_bits_equal(g2[2], orc.widen(w[int(bad[2])]), "get_rows valid id after bad ones")
+
+
 # --------------------------------------------------------------- C1: 576
 
 def test_576_parity_both_orders(orc):
