@@ -61,9 +61,12 @@ def lib() -> ctypes.CDLL:
         L.f16wm_mat_vec_multi_f32.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, P]
         L.f16wm_mat_mul.argtypes = [P, I64, I64, P, I64, P, P]
         L.f16wm_mat_mul_mfma.argtypes = [P, I64, I64, P, I64, P, P]
+        L.f16wm_mat_mul_multi.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, I64, P]
+        L.f16wm_mat_mul_mfma_multi.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, I64, P]
         L.f16wm_takes_sgemm.argtypes = [I64, I64, I64]
         for f in ("f16wm_to_f16", "f16wm_widen", "f16wm_get_rows", "f16wm_mat_vec", "f16wm_mat_vec_multi", "f16wm_mat_vec_f32",
-                  "f16wm_mat_vec_multi_f32", "f16wm_mat_mul", "f16wm_mat_mul_mfma", "f16wm_takes_sgemm"):
+                  "f16wm_mat_vec_multi_f32", "f16wm_mat_mul", "f16wm_mat_mul_mfma", "f16wm_mat_mul_multi",
+                  "f16wm_mat_mul_mfma_multi", "f16wm_takes_sgemm"):
             getattr(L, f).restype = ctypes.c_int
         L.f16wm_last_error.restype = ctypes.c_char_p
         L.f16wm_last_error.argtypes = []
@@ -263,3 +266,50 @@ def mat_mul(w: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = None) -
 def mat_mul_mfma(w: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """The same product on the fp16 matrix cores (approximate, f32 accumulation)."""
     return _mm(lib().f16wm_mat_mul_mfma, w, a, out)
+
+
+def _mm_multi(fn, ws, a, outs):
+    ws = list(ws)
+    if not 1 <= len(ws) <= MAX_MULTI:
+        raise ValueError("1..%d matrices" % MAX_MULTI)
+    k = None
+    for w in ws:
+        _, kk = _wk(w)
+        if k is None:
+            k = kk
+        elif kk != k:
+            raise ValueError("all matrices must share k")
+    _f16(a, "a")
+    if a.dim() == 1:
+        a = a.view(1, -1)
+    if a.dim() != 2 or a.shape[1] != k:
+        raise ValueError("a must be [n, k] with k = %d" % k)
+    n = a.shape[0]
+    if outs is None:
+        outs = [torch.empty((n, w.shape[0]), dtype=torch.float32, device=w.device) for w in ws]
+    outs = list(outs)
+    if len(outs) != len(ws):
+        raise ValueError("one output per matrix")
+    mats = (_Mat * len(ws))()
+    for i, (w, o) in enumerate(zip(ws, outs)):
+        _f32(o, "outs[%d]" % i)
+        if o.numel() != n * w.shape[0]:
+            raise ValueError("outs[%d] must have n*rows = %d elements" % (i, n * w.shape[0]))
+        mats[i].w = w.data_ptr()
+        mats[i].rows = w.shape[0]
+        mats[i].out = o.data_ptr()
+    dev = ws[0].device
+    with torch.cuda.device(dev):
+        _check(fn(mats, len(ws), k, a.data_ptr(), n, _stream(dev)))
+    return outs
+
+
+def mat_mul_multi(ws, a: torch.Tensor, outs=None) -> list:
+    """Exact products of several matrices (same k) with one activation block
+    [n, k]: one [n, rows_m] output each, each in its shape's order."""
+    return _mm_multi(lib().f16wm_mat_mul_multi, ws, a, outs)
+
+
+def mat_mul_mfma_multi(ws, a: torch.Tensor, outs=None) -> list:
+    """The MFMA products of several matrices (same k) with one activation block, one launch."""
+    return _mm_multi(lib().f16wm_mat_mul_mfma_multi, ws, a, outs)

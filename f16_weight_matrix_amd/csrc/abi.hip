@@ -202,6 +202,81 @@ int mat_vec_multi_impl(const char *fn, const f16wm_mat *mats, int32_t count, int
     return launched(fn, f16wm::launch_vec_dot(t, k, a, f32act, 1, vec8, (hipStream_t)stream));
 }
 
+// Products of `count` matrices sharing k and the activation block a [n][k]
+// (out of matrix m: [n][rows_m]).  Exact: each matrix in the order its own
+// shape picks (tinyBLAS when takes_sgemm(rows_m, k, n), else vec_dot); one
+// launch when every matrix takes the tinyBLAS order.  mfma: the matrix-core
+// product of every matrix in one launch.
+int mat_mul_impl(const char *fn, const f16wm_mat *mats, int32_t count, int64_t k, const uint16_t *a,
+                 int64_t n, bool mfma, void *stream)
+{
+    if (count < 1 || count > F16WM_MAX_MULTI)
+        return fail(F16WM_EINVAL, "%s: count %d outside 1..%d", fn, (int)count, F16WM_MAX_MULTI);
+    if (!mats) return fail(F16WM_EINVAL, "%s: null descriptor array", fn);
+    int64_t total = 0;
+    for (int m = 0; m < count; m++) {
+        int64_t we, ae, oe;
+        char name[80];
+        if (count == 1)
+            snprintf(name, sizeof name, "%s", fn);
+        else
+            snprintf(name, sizeof name, "%s[%d]", fn, m);
+        if (int rc = check_product(name, mats[m].w, mats[m].rows, k, a, 2, n, mats[m].out, &we, &ae, &oe))
+            return rc;
+        for (int j = 0; j < m; j++) {
+            const Span sm = span(mats[m].out, mats[m].rows * n * 4);
+            if (overlap(sm, span(mats[j].out, mats[j].rows * n * 4)) ||
+                overlap(sm, span(mats[j].w, mats[j].rows * k * 2)) ||
+                overlap(span(mats[j].out, mats[j].rows * n * 4), span(mats[m].w, mats[m].rows * k * 2)))
+                return fail(F16WM_EINVAL, "%s: outputs of matrices %d and %d overlap another array", fn,
+                            j, m);
+        }
+        total += mats[m].rows;
+    }
+    bool al16 = aligned(a, 16);
+    for (int m = 0; m < count; m++) al16 = al16 && aligned(mats[m].w, 16);
+    if (mfma && (k % 8 != 0 || !al16))
+        return fail(F16WM_EUNSUPPORTED, "%s: needs k %% 8 == 0 and 16-byte aligned w and a (k=%lld)", fn,
+                    (long long)k);
+    if (total == 0 || n == 0) return ok();
+    if (int rc = check_device(fn)) return rc;
+
+    f16wm::GemmTable g = {};
+    bool all_sgemm = true;
+    for (int m = 0; m < count; m++) {
+        if (mats[m].rows == 0) continue;
+        g.w[g.count] = mats[m].w;
+        g.rows[g.count] = mats[m].rows;
+        g.out[g.count] = mats[m].out;
+        g.count++;
+        all_sgemm = all_sgemm && f16wm_takes_sgemm(mats[m].rows, k, n);
+    }
+    if (mfma) return launched(fn, f16wm::launch_mfma(g, k, a, n, (hipStream_t)stream));
+    if (all_sgemm) return launched(fn, f16wm::launch_sgemm(g, k, a, n, al16, (hipStream_t)stream));
+    // other orders: one launch per matrix, each in its own order
+    for (int m = 0; m < g.count; m++) {
+        hipError_t e;
+        if (f16wm_takes_sgemm(g.rows[m], k, n)) {
+            f16wm::GemmTable one = {};
+            one.count = 1;
+            one.w[0] = g.w[m];
+            one.rows[0] = g.rows[m];
+            one.out[0] = g.out[m];
+            e = f16wm::launch_sgemm(one, k, a, n, al16, (hipStream_t)stream);
+        } else {
+            f16wm::RowTable t = {};
+            t.count = 1;
+            t.w[0] = g.w[m];
+            t.out[0] = g.out[m];
+            t.row0[0] = 0;
+            t.row0[1] = g.rows[m];
+            e = f16wm::launch_vec_dot(t, k, a, false, n, k % 8 == 0 && al16, (hipStream_t)stream);
+        }
+        if (e != hipSuccess) return launched(fn, e);
+    }
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -269,36 +344,27 @@ int f16wm_mat_vec_multi_f32(const f16wm_mat *mats, int32_t count, int64_t k, con
 int f16wm_mat_mul(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
                   float *out, void *stream)
 {
-    const char *fn = "f16wm_mat_mul";
-    int64_t we, ae, oe;
-    if (int rc = check_product(fn, w, rows, k, a, 2, n, out, &we, &ae, &oe)) return rc;
-    if (rows == 0 || n == 0) return ok();
-    if (int rc = check_device(fn)) return rc;
-    const bool al16 = aligned(w, 16) && aligned(a, 16);
-    if (f16wm_takes_sgemm(rows, k, n))
-        return launched(fn, f16wm::launch_sgemm(w, rows, k, a, n, out, al16, (hipStream_t)stream));
-    f16wm::RowTable t = {};
-    t.count = 1;
-    t.w[0] = w;
-    t.out[0] = out;
-    t.row0[0] = 0;
-    t.row0[1] = rows;
-    const bool vec8 = k % 8 == 0 && al16;
-    return launched(fn, f16wm::launch_vec_dot(t, k, a, false, n, vec8, (hipStream_t)stream));
+    const f16wm_mat m = {w, rows, out};
+    return mat_mul_impl("f16wm_mat_mul", &m, 1, k, a, n, false, stream);
+}
+
+int f16wm_mat_mul_multi(const f16wm_mat *mats, int32_t count, int64_t k, const uint16_t *a, int64_t n,
+                        void *stream)
+{
+    return mat_mul_impl("f16wm_mat_mul_multi", mats, count, k, a, n, false, stream);
 }
 
 int f16wm_mat_mul_mfma(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
                        float *out, void *stream)
 {
-    const char *fn = "f16wm_mat_mul_mfma";
-    int64_t we, ae, oe;
-    if (int rc = check_product(fn, w, rows, k, a, 2, n, out, &we, &ae, &oe)) return rc;
-    if (k % 8 != 0 || !aligned(w, 16) || !aligned(a, 16))
-        return fail(F16WM_EUNSUPPORTED, "%s: needs k %% 8 == 0 and 16-byte aligned w and a (k=%lld)", fn,
-                    (long long)k);
-    if (rows == 0 || n == 0) return ok();
-    if (int rc = check_device(fn)) return rc;
-    return launched(fn, f16wm::launch_mfma(w, rows, k, a, n, out, (hipStream_t)stream));
+    const f16wm_mat m = {w, rows, out};
+    return mat_mul_impl("f16wm_mat_mul_mfma", &m, 1, k, a, n, true, stream);
+}
+
+int f16wm_mat_mul_mfma_multi(const f16wm_mat *mats, int32_t count, int64_t k, const uint16_t *a,
+                             int64_t n, void *stream)
+{
+    return mat_mul_impl("f16wm_mat_mul_mfma_multi", mats, count, k, a, n, true, stream);
 }
 
 }  // extern "C"

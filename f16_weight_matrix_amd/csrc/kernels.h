@@ -17,6 +17,39 @@ struct RowTable {
     int32_t count;
 };
 
+// Products of up to F16WM_MAX_MULTI weight matrices that share k and one
+// activation block A [n][k]: matrix m has rows[m] rows and output out[m]
+// ([n][rows[m]]).  tile0[m] is the first output tile of matrix m (filled by
+// the launcher for its tile size), so one launch covers every matrix.
+struct GemmTable {
+    const uint16_t *w[F16WM_MAX_MULTI];
+    float *out[F16WM_MAX_MULTI];
+    int64_t rows[F16WM_MAX_MULTI];
+    int32_t tile0[F16WM_MAX_MULTI + 1];
+    int32_t count;
+};
+
+// The output tile `t` of a grouped product with `nct` column tiles: its
+// matrix, row tile and column tile.
+__device__ __forceinline__ void gemm_tile(const GemmTable &g, int t, int nct, int &m, int &rt, int &ct)
+{
+    m = 0;
+#pragma unroll
+    for (int i = 1; i < F16WM_MAX_MULTI; i++)
+        if (i < g.count && t >= g.tile0[i]) m = i;
+    const int local = t - g.tile0[m];
+    rt = local / nct;
+    ct = local % nct;
+}
+
+// Block b of a grid of `ntiles` blocks runs on XCD b % 8 (round-robin
+// dispatch); this hands each XCD a contiguous range of tiles.
+__device__ __forceinline__ int xcd_tile(int b, int ntiles)
+{
+    const int xcd = b & 7, pos = b >> 3, q = ntiles >> 3, rem = ntiles & 7;
+    return xcd * q + (xcd < rem ? xcd : rem) + pos;
+}
+
 // Every launcher enqueues on `stream` and returns the hipError_t of the launch.
 hipError_t launch_to_f16(const float *x, uint16_t *y, int64_t count, hipStream_t stream);
 
@@ -28,10 +61,10 @@ hipError_t launch_to_f16(const float *x, uint16_t *y, int64_t count, hipStream_t
 hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32act, int64_t ncols,
                           bool vec8, hipStream_t stream);
 
-// tinyBLAS order (rows % 4 == 0, k % 8 == 0, n >= 2 checked by the caller).
-// aligned16: w and a are 16-byte aligned.
-hipError_t launch_sgemm(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
-                        float *out, bool aligned16, hipStream_t stream);
+// tinyBLAS order for every matrix of g (rows % 4 == 0, k % 8 == 0, n >= 2
+// checked by the caller).  aligned16: every w and a are 16-byte aligned.
+hipError_t launch_sgemm(GemmTable g, int64_t k, const uint16_t *a, int64_t n, bool aligned16,
+                        hipStream_t stream);
 
 // Exact f16 -> f32 of count values, and of rows ids[0..nids) of W (rows x k)
 // into out[nids][k] (an id outside [0, rows) gives a row of NaN).
@@ -39,8 +72,8 @@ hipError_t launch_widen(const uint16_t *h, float *y, int64_t count, hipStream_t 
 hipError_t launch_get_rows(const uint16_t *w, int64_t rows, int64_t k, const int64_t *ids, int64_t nids,
                            float *out, hipStream_t stream);
 
-// fp16 MFMA product (k % 8 == 0, w and a 16-byte aligned).
-hipError_t launch_mfma(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
-                       float *out, hipStream_t stream);
+// fp16 MFMA product of every matrix of g (k % 8 == 0, w and a 16-byte
+// aligned).
+hipError_t launch_mfma(GemmTable g, int64_t k, const uint16_t *a, int64_t n, hipStream_t stream);
 
 }  // namespace f16wm

@@ -37,10 +37,8 @@ constexpr int kKS = 32;          // k per stage
 constexpr int kLD = kKS + 8;     // padded LDS row, in halves (80 bytes)
 
 template <int BM, int BN>
-__global__ __launch_bounds__(256) void mfma_generic(const uint16_t *__restrict__ w, int64_t rows,
-                                                   int64_t k, const uint16_t *__restrict__ a,
-                                                   int64_t n, float *__restrict__ out, int nrt,
-                                                   int nct)
+__global__ __launch_bounds__(256) void mfma_generic(GemmTable g, int64_t k, const uint16_t *__restrict__ a,
+                                                    int64_t n, int nct)
 {
     constexpr int WM = BM / 2, WN = BN / 2;       // wave tile
     constexpr int TM = WM / 32, TN = WN / 32;     // 32x32 MFMA tiles per wave
@@ -51,13 +49,15 @@ __global__ __launch_bounds__(256) void mfma_generic(const uint16_t *__restrict__
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][kLD];
     __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN][kLD];
 
-    // XCD-aware tile index (blocks are dispatched round-robin over 8 XCDs).
-    const int ntiles = nrt * nct;
-    const int b = blockIdx.x;
-    const int xcd = b & 7, pos = b >> 3, q = ntiles >> 3, rem = ntiles & 7;
-    const int t = xcd * q + (xcd < rem ? xcd : rem) + pos;
-    const int64_t r0 = (int64_t)(t / nct) * BN;
-    const int64_t c0 = (int64_t)(t % nct) * BM;
+    // XCD-aware tile index (blocks are dispatched round-robin over 8 XCDs),
+    // then this tile's matrix.
+    int mi, rt, ct;
+    gemm_tile(g, xcd_tile(blockIdx.x, g.tile0[g.count]), nct, mi, rt, ct);
+    const uint16_t *__restrict__ w = g.w[mi];
+    const int64_t rows = g.rows[mi];
+    float *__restrict__ out = g.out[mi];
+    const int64_t r0 = (int64_t)rt * BN;
+    const int64_t c0 = (int64_t)ct * BM;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -192,9 +192,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base
 }
 
 template <int BM, int BN>
-__global__ __launch_bounds__(256) void mfma_fast(const uint16_t *__restrict__ w, int64_t rows, int64_t k,
-                                                 const uint16_t *__restrict__ a, int64_t n,
-                                                 float *__restrict__ out, int nrt, int nct)
+__global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const uint16_t *__restrict__ a,
+                                                 int64_t n, int nct)
 {
     constexpr int WM = BM / 2, WN = BN / 2;       // wave tile
     constexpr int TM = WM / 32, TN = WN / 32;     // 32x32 MFMA tiles per wave
@@ -204,12 +203,15 @@ __global__ __launch_bounds__(256) void mfma_fast(const uint16_t *__restrict__ w,
     constexpr int BUFH = (BM + BN) * ROWH;        // halves per LDS buffer
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUFH];
 
-    const int ntiles = nrt * nct;
-    const int b = blockIdx.x;
-    const int xcd = b & 7, pos = b >> 3, q = ntiles >> 3, rem = ntiles & 7;
-    const int t = xcd * q + (xcd < rem ? xcd : rem) + pos;
-    const int64_t r0 = (int64_t)(t / nct) * BN;
-    const int64_t c0 = (int64_t)(t % nct) * BM;
+    // XCD-aware tile index (blocks are dispatched round-robin over 8 XCDs),
+    // then this tile's matrix.
+    int mi, rt, ct;
+    gemm_tile(g, xcd_tile(blockIdx.x, g.tile0[g.count]), nct, mi, rt, ct);
+    const uint16_t *__restrict__ w = g.w[mi];
+    const int64_t rows = g.rows[mi];
+    float *__restrict__ out = g.out[mi];
+    const int64_t r0 = (int64_t)rt * BN;
+    const int64_t c0 = (int64_t)ct * BM;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -319,41 +321,42 @@ __global__ __launch_bounds__(256) void mfma_fast(const uint16_t *__restrict__ w,
         }
 }
 
-template <int BM, int BN>
-hipError_t launch_tiles(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
-                        float *out, hipStream_t stream)
+// Tile offsets of every matrix for a B x B tiling; false past grid.x.
+bool fill_tiles(GemmTable &g, int64_t n, int B, int64_t *nct_out)
 {
-    const int64_t nrt = (rows + BN - 1) / BN;
-    const int64_t nct = (n + BM - 1) / BM;
-    if (nrt * nct > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
-    mfma_generic<BM, BN><<<dim3((uint32_t)(nrt * nct)), dim3(256), 0, stream>>>(w, rows, k, a, n, out,
-                                                                           (int)nrt, (int)nct);
-    return hipGetLastError();
+    const int64_t nct = (n + B - 1) / B;
+    int64_t tiles = 0;
+    for (int i = 0; i < g.count; i++) {
+        g.tile0[i] = (int32_t)tiles;
+        tiles += (g.rows[i] + B - 1) / B * nct;
+        if (tiles > 0x7fffffff) return false;
+    }
+    g.tile0[g.count] = (int32_t)tiles;
+    *nct_out = nct;
+    return true;
 }
 
 }  // namespace
 
-hipError_t launch_mfma(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
-                       float *out, hipStream_t stream)
+hipError_t launch_mfma(GemmTable g, int64_t k, const uint16_t *a, int64_t n, hipStream_t stream)
 {
     // 256 x 256 tiles when they still give at least one block per CU,
     // 128 x 128 otherwise.  The fast kernel needs k % 64 == 0 and 32-bit
     // byte offsets inside one 256-row tile.
-    const int64_t big = ((rows + 255) / 256) * ((n + 255) / 256);
+    int64_t big = 0;
+    for (int i = 0; i < g.count; i++) big += ((g.rows[i] + 255) / 256) * ((n + 255) / 256);
     const bool fast = k % kFKS == 0 && k > 0 && 256 * k * 2 < ((int64_t)1 << 31);
-    if (fast) {
-        const bool use_big = big >= 256;
-        const int B = use_big ? 256 : 128;
-        const int64_t nrt = (rows + B - 1) / B, nct = (n + B - 1) / B;
-        if (nrt * nct > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
-        const dim3 grid((uint32_t)(nrt * nct));
-        if (use_big)
-            mfma_fast<256, 256><<<grid, dim3(256), 0, stream>>>(w, rows, k, a, n, out, (int)nrt, (int)nct);
-        else
-            mfma_fast<128, 128><<<grid, dim3(256), 0, stream>>>(w, rows, k, a, n, out, (int)nrt, (int)nct);
-        return hipGetLastError();
-    }
-    return launch_tiles<128, 128>(w, rows, k, a, n, out, stream);
+    const int B = fast && big >= 256 ? 256 : 128;
+    int64_t nct = 0;
+    if (!fill_tiles(g, n, B, &nct)) return hipErrorInvalidConfiguration;
+    const dim3 grid((uint32_t)g.tile0[g.count]);
+    if (!fast)
+        mfma_generic<128, 128><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+    else if (B == 256)
+        mfma_fast<256, 256><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+    else
+        mfma_fast<128, 128><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+    return hipGetLastError();
 }
 
 }  // namespace f16wm

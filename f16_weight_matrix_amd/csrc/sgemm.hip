@@ -97,20 +97,19 @@ __device__ __forceinline__ void stash_unit(f32x4 *op, u32x4 v, int r, int t)
 }
 
 template <bool kAligned>
-__global__ __launch_bounds__(256) void sgemm_kernel(const uint16_t *__restrict__ w, int64_t rows,
-                                                    int64_t k, const uint16_t *__restrict__ a,
-                                                    int64_t n, float *__restrict__ out, int nrt,
-                                                    int nct)
+__global__ __launch_bounds__(256) void sgemm_kernel(GemmTable g, int64_t k, const uint16_t *__restrict__ a,
+                                                    int64_t n, int nct)
 {
     __shared__ f32x4 lds[2][2 * kOp];    // [buffer][weights | activations]
 
-    // XCD-aware tile index
-    const int ntiles = nrt * nct;
-    const int b = blockIdx.x;
-    const int xcd = b & 7, pos = b >> 3, qq = ntiles >> 3, rem = ntiles & 7;
-    const int tile = xcd * qq + (xcd < rem ? xcd : rem) + pos;
-    const int64_t row0 = (int64_t)(tile / nct) * kBM;
-    const int64_t col0 = (int64_t)(tile % nct) * kBN;
+    // XCD-aware tile index, then this tile's matrix
+    int mi, rt, ct;
+    gemm_tile(g, xcd_tile(blockIdx.x, g.tile0[g.count]), nct, mi, rt, ct);
+    const uint16_t *__restrict__ w = g.w[mi];
+    const int64_t rows = g.rows[mi];
+    float *__restrict__ out = g.out[mi];
+    const int64_t row0 = (int64_t)rt * kBM;
+    const int64_t col0 = (int64_t)ct * kBN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -189,17 +188,22 @@ __global__ __launch_bounds__(256) void sgemm_kernel(const uint16_t *__restrict__
 
 }  // namespace
 
-hipError_t launch_sgemm(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
-                        float *out, bool aligned16, hipStream_t stream)
+hipError_t launch_sgemm(GemmTable g, int64_t k, const uint16_t *a, int64_t n, bool aligned16,
+                        hipStream_t stream)
 {
-    const int64_t nrt = (rows + kBM - 1) / kBM;
     const int64_t nct = (n + kBN - 1) / kBN;
-    if (nrt * nct > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
-    const dim3 grid((uint32_t)(nrt * nct));
+    int64_t tiles = 0;
+    for (int i = 0; i < g.count; i++) {
+        g.tile0[i] = (int32_t)tiles;
+        tiles += (g.rows[i] + kBM - 1) / kBM * nct;
+        if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
+    }
+    g.tile0[g.count] = (int32_t)tiles;
+    const dim3 grid((uint32_t)tiles);
     if (aligned16)
-        sgemm_kernel<true><<<grid, dim3(256), 0, stream>>>(w, rows, k, a, n, out, (int)nrt, (int)nct);
+        sgemm_kernel<true><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
     else
-        sgemm_kernel<false><<<grid, dim3(256), 0, stream>>>(w, rows, k, a, n, out, (int)nrt, (int)nct);
+        sgemm_kernel<false><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
     return hipGetLastError();
 }
 

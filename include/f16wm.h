@@ -133,6 +133,19 @@ int f16wm_mat_mul(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a,
                   float *out, void *stream);
 
 /*
+ * f16wm_mat_mul_multi: f16wm_mat_mul for each of `count` matrices
+ * (1..F16WM_MAX_MULTI) that share k and the activation block a [n][k]:
+ * mats[m].out is n x mats[m].rows f32.  Each matrix takes the order its own
+ * shape picks (f16wm_takes_sgemm(mats[m].rows, k, n)); when every matrix takes
+ * the tinyBLAS order the whole group is one launch.  The grouping follows the
+ * shared activations of bankML page "bankML/forward.rs" (Advantages and
+ * efficiency: one rounded activation feeds Q, K and V, another gate and up)
+ * for prefill micro-batches.  `mats` is a HOST array read during the call.
+ */
+int f16wm_mat_mul_multi(const f16wm_mat *mats, int32_t count, int64_t k, const uint16_t *a, int64_t n,
+                        void *stream);
+
+/*
  * f16wm_mat_mul_mfma: the same product and layout as f16wm_mat_mul computed on
  * the fp16 matrix cores (MFMA, f16 x f16 products, f32 accumulation).  An
  * approximate fast path for prefill micro-batches (bankML page
@@ -143,6 +156,11 @@ int f16wm_mat_mul(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a,
  */
 int f16wm_mat_mul_mfma(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
                        float *out, void *stream);
+
+/* f16wm_mat_mul_mfma_multi: f16wm_mat_mul_mfma for a group of matrices that
+   share k and a (as f16wm_mat_mul_multi), in one launch. */
+int f16wm_mat_mul_mfma_multi(const f16wm_mat *mats, int32_t count, int64_t k, const uint16_t *a,
+                             int64_t n, void *stream);
 
 /*
  * f16wm_takes_sgemm: 1 when n >= 2 && rows % 4 == 0 && k % 8 == 0, else 0

@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     assert _declared() == sorted([
         "f16wm_to_f16", "f16wm_widen", "f16wm_get_rows", "f16wm_mat_vec", "f16wm_mat_vec_multi",
         "f16wm_mat_vec_f32", "f16wm_mat_vec_multi_f32", "f16wm_mat_mul", "f16wm_mat_mul_mfma",
-        "f16wm_takes_sgemm", "f16wm_last_error", "f16wm_version"])
+        "f16wm_mat_mul_multi", "f16wm_mat_mul_mfma_multi", "f16wm_takes_sgemm", "f16wm_last_error",
+        "f16wm_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -116,6 +117,22 @@ def test_mat_mul_rejects_bad_arguments(L):
     assert "overlap" in _err(L.f16wm_mat_mul(P, 4, 8, P + 4096, 3, P + 4100, STREAM))
     assert "null" in _err(L.f16wm_mat_mul(P, 4, 8, None, 3, P + 8192, STREAM))
     assert "too large" in _err(L.f16wm_mat_mul(P, 1 << 21, 8, P, 1 << 21, P, STREAM))
+
+
+def test_grouped_products_reject_bad_arguments(L):
+    Mat = f16wm._Mat
+    mats = (Mat * 2)()
+    mats[0].w, mats[0].rows, mats[0].out = P, 4, P + (1 << 20)
+    mats[1].w, mats[1].rows, mats[1].out = P + 4096, 4, P + (1 << 20) + 16   # overlaps out[0] (n=3)
+    assert "overlap" in _err(L.f16wm_mat_mul_multi(mats, 2, 8, P + (1 << 21), 3, STREAM))
+    assert "count" in _err(L.f16wm_mat_mul_multi(mats, 0, 8, P + (1 << 21), 3, STREAM))
+    assert "null" in _err(L.f16wm_mat_mul_mfma_multi(None, 2, 8, P + (1 << 21), 3, STREAM))
+    mats[1].out = P + (1 << 20) + 4096
+    rc = L.f16wm_mat_mul_mfma_multi(mats, 2, 12, P + (1 << 21), 3, STREAM)
+    assert rc == f16wm.F16WM_EUNSUPPORTED
+    mats[1].rows = 0
+    mats[0].rows = 0
+    assert L.f16wm_mat_mul_multi(mats, 2, 8, P + (1 << 21), 3, STREAM) == 0
 
 
 def test_mat_mul_mfma_rejects_unsupported(L):

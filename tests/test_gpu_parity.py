@@ -302,6 +302,42 @@ def test_f32_activation_multi(orc, shapes):
         assert_bits_equal(o.cpu().numpy(), orc.mat_vec(w, x16), "multi f32 matrix %d" % i)
 
 
+# ------------------------------------------------------ grouped products
+
+@pytest.mark.parametrize("shapes,n", [
+    ([(576, 576), (192, 576), (192, 576)], 512),      # 135M Q/K/V, one prefill micro-batch
+    ([(1536, 576), (1536, 576)], 512),                # 135M gate/up
+    ([(12, 100), (13, 100), (16, 100)], 5),           # mixed orders: 13 rows falls back to vec_dot
+    ([(4, 40), (100, 40)], 1),                        # one column: vec_dot
+    ([(1000, 64), (0, 64), (24, 64)], 70),            # an empty matrix in the group
+])
+def test_grouped_exact_products(orc, shapes, n):
+    k = shapes[0][1]
+    ws = [synth.random_f16((91, i, r, k), (r, k), 0.02) for i, (r, _) in enumerate(shapes)]
+    a = synth.random_f16((92, k, n), (n, k))
+    outs = f16wm.mat_mul_multi([up16(w) for w in ws], up16(a))
+    for i, (w, o) in enumerate(zip(ws, outs)):
+        assert_bits_equal(o.cpu().numpy(), orc.mat_mul(w, a), "grouped exact matrix %d %s n=%d" % (i, shapes[i], n))
+
+
+@pytest.mark.parametrize("shapes,n", [
+    ([(4096, 4096), (1024, 4096), (1024, 4096)], 512),
+    ([(576, 576), (192, 576), (192, 576)], 512),
+    ([(200, 40), (13, 40)], 77),
+])
+def test_grouped_mfma_products(orc, shapes, n):
+    k = shapes[0][1]
+    ws = [synth.random_f16((93, i, r, k), (r, k), 0.02) for i, (r, _) in enumerate(shapes)]
+    a = synth.random_f16((94, k, n), (n, k))
+    outs = f16wm.mat_mul_mfma_multi([up16(w) for w in ws], up16(a))
+    rng = np.random.default_rng(3)
+    for i, (w, o) in enumerate(zip(ws, outs)):
+        rows = w.shape[0]
+        rr, cc = rng.integers(0, rows, 3000), rng.integers(0, n, 3000)
+        e, _ = mfma_error(orc, w, a, o.cpu().numpy(), rr, cc)
+        assert e <= MFMA_TOL, (i, e)
+
+
 # ---------------------------------------------------------- edge cases
 
 def test_degenerate_sizes(orc):
