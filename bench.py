@@ -208,7 +208,7 @@ def main():
     gemv_all_ms = sum(sum(r) for r in gemv_ms) / K
 
     rec = traffic_record(os.path.join(ROOT, "f16_weight_matrix_amd", "csrc", "vec_dot.hip"))
-    traffic = rec.get("bytes_per_launch") if rec and rec.get("kernel") == "vec_dot_lds<4>" else None
+    traffic = rec.get("bytes_per_launch") if rec and rec.get("kernel") == "vec_dot_lds<4, true, true>" else None
 
     # Next row beside the step: the embedding lookup of a 512-token micro-batch
     # from the tied 128256x4096 table (get_rows), timed on its own.
@@ -251,7 +251,7 @@ def main():
         "phases_ms": {"decode": round(dec_avg, 4), "prefill_exact": round(exact_avg, 4),
                       "prefill_mfma": round(mfma_avg, 4)},
         "roofline": {
-            "kernel": "vec_dot_lds<4> (logits GEMV 128256x4096, vec_dot order)",
+            "kernel": "vec_dot_lds<4, true, true> (logits GEMV 128256x4096, f32 column rounded in staging, vec_dot order)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
