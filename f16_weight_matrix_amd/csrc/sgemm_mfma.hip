@@ -1,0 +1,370 @@
+// tinyBLAS order on the fp32 matrix cores: the exact product for n >= 2
+// columns when rows % 4 == 0 and k % 8 == 0.
+//
+// bankML f16 page, Design notes ("sgemm_dot" and "Blocking"): every output
+// element is ONE chain of eight f32 lanes, lane l taking elements 8t + l in
+// ascending t, each step an FMA; the element is then reduced
+// ((l0 + l4) + (l2 + l6)) + ((l1 + l5) + (l3 + l7)).  Matrix products
+// (mat_mul_par): out[c*rows + r].
+//
+// gfx950 design.  v_mfma_f32_32x32x1_2b_f32 computes, for two independent
+// blocks, D[i][j] = C[i][j] + A[i] * B[j] over a 32 x 32 tile: one rank-1
+// update per instruction, i.e. one chain step for 1024 elements of a block.
+// On this GPU that update is the IEEE binary32 sum of C and the product,
+// rounded to nearest even (an f16 x f16 product is exact in binary32, so
+// this is the FMA step of the chain bit for bit; signed zeros, infinities,
+// NaNs and subnormal accumulators behave as IEEE says).  So:
+//  - block 0 of instruction p (p = 0..3) holds chain lane p and block 1 holds
+//    chain lane p + 4: for step t the A operand is W[row][8t + p] in lanes
+//    0..31 and W[row][8t + 4 + p] in lanes 32..63, the B operand the same
+//    elements of the activation columns.  Each thread therefore needs four
+//    consecutive values of its row (or column) per step: one 16-byte LDS
+//    read once they are f32.
+//  - The eight lanes of an element end in the same thread (instruction p,
+//    registers v and v + 16), so the hsum is four in-thread adds in the
+//    page's order, no shuffles.
+//  - A 256-thread block computes 64 weight rows x 128 columns; each wave
+//    32 rows x 64 columns = two 32-column tiles x four instructions x 32
+//    accumulators = 256 accumulators (AGPRs), one wave per SIMD.  Per step a
+//    wave issues eight MFMAs from three 16-byte LDS reads, read one step
+//    ahead so their latency hides behind the matrix core.
+//  - k is staged 64 at a time (8 chain steps) through two LDS buffers holding
+//    the operands already widened to f32 (exactly, once per element and
+//    block): widening inside the step loop would put 24 conversions between
+//    every 16 MFMAs and keep the matrix core a quarter idle.
+//  - Global loads run a stage ahead of their stash and two ahead of their
+//    MFMAs: while stage st computes, stage st + 1's chunks (in registers) are
+//    widened and written to the other buffer between the MFMAs, a few at a
+//    time, and each register is refilled with its chunk of stage st + 2.
+//    Aligned operands use raw buffer loads whose resource covers only this
+//    tile; an offset past its end reads zero, so rows past the matrix,
+//    columns past n and chunks past k (k % 8 == 0: a chunk is all in or all
+//    out) need no branch, and the loop waits on precise load counts.
+//  - Zero chunks past k are harmless: the step C + 0 * 0 leaves every
+//    accumulator unchanged because an accumulator starting at +0 never
+//    becomes -0.  Rows past `rows` and columns past n are not stored.
+//  - Blocks walk the output tiles in an XCD-aware order (block b runs on
+//    XCD b % 8, each XCD takes a contiguous range of tiles, the column tiles
+//    of one weight-row block are consecutive), so each weight row block is
+//    read from HBM once and re-read from that XCD's L2.
+//
+// Matrix-core bound: rows*n*k chain steps = 2*rows*n*k flops at the fp32
+// MFMA rate.
+#include "kernels.h"
+
+#include <type_traits>
+
+namespace f16wm {
+namespace {
+
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+constexpr int kBM = 64;                   // weight rows per block
+constexpr int kBN = 128;                  // activation columns per block
+constexpr int kKS = 64;                   // k per stage
+constexpr int kSteps = kKS / 8;           // chain steps per stage
+constexpr int kWG = kBM * 16 + 16;        // bytes of one (step, half) group, weights
+constexpr int kXG = kBN * 16 + 16;        // bytes of one (step, half) group, activations
+constexpr int kWBuf = 2 * kSteps * kWG;   // bytes of one weight buffer
+constexpr int kXBuf = 2 * kSteps * kXG;   // bytes of one activation buffer
+constexpr int kWPT = kBM * kSteps / 256;  // 16-byte weight chunks per thread
+constexpr int kXPT = kBN * kSteps / 256;  // 16-byte activation chunks per thread
+static_assert(kWPT * 256 == kBM * kSteps && kXPT * 256 == kBN * kSteps, "chunks must divide evenly");
+
+template <bool kAligned>
+__device__ __forceinline__ u32x4 load8(const uint16_t *p)
+{
+    if (kAligned) return *reinterpret_cast<const u32x4 *>(p);
+    u32x4 v;
+    v.x = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
+    v.y = (uint32_t)p[2] | ((uint32_t)p[3] << 16);
+    v.z = (uint32_t)p[4] | ((uint32_t)p[5] << 16);
+    v.w = (uint32_t)p[6] | ((uint32_t)p[7] << 16);
+    return v;
+}
+
+// Where a stage's chunks come from.  kBuf: 16-byte aligned operands and
+// kBN * k * 2 < 2^31 bytes, read with raw buffer loads whose resource covers
+// just this tile's rows (or columns); an offset at or past the resource's
+// end returns zero, so rows past the matrix, columns past n and chunks past
+// k need no branch.  Otherwise plain loads guarded by the same conditions.
+template <bool kBuf>
+struct Src {
+    const uint16_t *w, *a;
+    int64_t rows, n, k, row0, col0;
+    __amdgpu_buffer_rsrc_t rw, rx;
+
+    __device__ __forceinline__ Src(const uint16_t *w_, int64_t rows_, const uint16_t *a_, int64_t n_, int64_t k_,
+                                   int64_t row0_, int64_t col0_)
+        : w(w_), a(a_), rows(rows_), n(n_), k(k_), row0(row0_), col0(col0_)
+    {
+        if constexpr (kBuf) {
+            const int64_t wr = rows - row0 < kBM ? rows - row0 : kBM;
+            const int64_t xr = n - col0 < kBN ? n - col0 : kBN;
+            // raw buffer: stride 0, num_records = bytes, gfx9 dword3
+            rw = __builtin_amdgcn_make_buffer_rsrc((void *)(w + row0 * k), (short)0, (int)(wr * k * 2), 0x00020000);
+            rx = __builtin_amdgcn_make_buffer_rsrc((void *)(a + col0 * k), (short)0, (int)(xr * k * 2), 0x00020000);
+        }
+    }
+
+    // Byte offset of chunk (r, gk) in a tile resource; a chunk past k gets
+    // bit 31 set, which puts it past the resource's end (under 2^31 bytes).
+    __device__ __forceinline__ uint32_t offset(int r, int64_t gk) const
+    {
+        return (uint32_t)((r * k + gk) * 2) | (gk < k ? 0u : 0x80000000u);
+    }
+
+    // chunk (r, elements gk .. gk + 7) of the weight tile / activation tile
+    __device__ __forceinline__ u32x4 wchunk(int r, int64_t gk) const
+    {
+        if constexpr (kBuf) {
+            return __builtin_amdgcn_raw_buffer_load_b128(rw, (int)offset(r, gk), 0, 0);
+        } else {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row0 + r < rows && gk < k) v = load8<false>(w + (row0 + r) * k + gk);
+            return v;
+        }
+    }
+    __device__ __forceinline__ u32x4 xchunk(int r, int64_t gk) const
+    {
+        if constexpr (kBuf) {
+            return __builtin_amdgcn_raw_buffer_load_b128(rx, (int)offset(r, gk), 0, 0);
+        } else {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (col0 + r < n && gk < k) v = load8<false>(a + (col0 + r) * k + gk);
+            return v;
+        }
+    }
+};
+
+// Global -> registers for the stage at k0.  Chunk c of a tile is row (or
+// column) c / kSteps, elements 8 (c % kSteps) .. + 7 of the stage; zero past
+// rows, n or k (k % 8 == 0: a chunk is all inside k or all outside).
+template <bool kBuf>
+__device__ __forceinline__ void fetch_stage(u32x4 (&wr)[kWPT], u32x4 (&xr)[kXPT], const Src<kBuf> &src,
+                                            int64_t k0, int tid)
+{
+#pragma unroll
+    for (int p = 0; p < kWPT; p++) {
+        const int c = p * 256 + tid;
+        wr[p] = src.wchunk(c / kSteps, k0 + 8 * (c % kSteps));
+    }
+#pragma unroll
+    for (int p = 0; p < kXPT; p++) {
+        const int c = p * 256 + tid;
+        xr[p] = src.xchunk(c / kSteps, k0 + 8 * (c % kSteps));
+    }
+}
+
+// Chunk j (weights first) of the stage at k0 into its register.
+template <bool kBuf, int j>
+__device__ __forceinline__ void fetch_chunk(u32x4 (&wr)[kWPT], u32x4 (&xr)[kXPT], const Src<kBuf> &src, int64_t k0,
+                                            int tid)
+{
+    constexpr bool isw = j < kWPT;
+    const int c = (isw ? j : j - kWPT) * 256 + tid;
+    if constexpr (isw)
+        wr[isw ? j : 0] = src.wchunk(c / kSteps, k0 + 8 * (c % kSteps));
+    else
+        xr[isw ? 0 : j - kWPT] = src.xchunk(c / kSteps, k0 + 8 * (c % kSteps));
+}
+
+// Registers -> LDS, widened exactly to f32 once here.  Entry (t, h, row) is
+// 16 bytes: elements 8t + 4h .. + 3 of one row, the four values a thread
+// feeds to the four instructions of step t; rows are contiguous, so a
+// half-wave reads 512 contiguous bytes, and the 16-byte pad per group puts
+// the eight steps of one row, written by eight neighbouring lanes, in eight
+// different bank groups.  Half q (0 .. kHalves - 1) is one entry: chunk q / 2
+// (weights first), elements 4 (q % 2) .. + 3.
+constexpr int kHalves = 2 * (kWPT + kXPT);
+
+template <int q>
+__device__ __forceinline__ void stash_half(char *wl, char *xl, const u32x4 (&wr)[kWPT], const u32x4 (&xr)[kXPT],
+                                           int tid)
+{
+    constexpr int cq = q / 2, hf = q % 2;
+    constexpr bool isw = cq < kWPT;
+    const int c = (isw ? cq : cq - kWPT) * 256 + tid;
+    const int r = c / kSteps, t = c % kSteps;
+    const half8 x = __builtin_bit_cast(half8, isw ? wr[isw ? cq : 0] : xr[isw ? 0 : cq - kWPT]);
+    char *grp = isw ? wl : xl;
+    const int gsize = isw ? kWG : kXG;
+    *reinterpret_cast<f32x4 *>(grp + (2 * t + hf) * gsize + r * 16) =
+        f32x4{(float)x[4 * hf], (float)x[4 * hf + 1], (float)x[4 * hf + 2], (float)x[4 * hf + 3]};
+}
+
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+__device__ __forceinline__ void stash_stage(char *wl, char *xl, const u32x4 (&wr)[kWPT],
+                                            const u32x4 (&xr)[kXPT], int tid)
+{
+    static_for<0, kHalves>([&](auto qc) { stash_half<decltype(qc)::value>(wl, xl, wr, xr, tid); });
+}
+
+// The stage's 4 * kSteps MFMA slots (step t, instruction p) share out the
+// kHalves stash entries evenly: entry q goes after slot q * 4 kSteps / kHalves.
+template <int t, int p>
+struct Slot {
+    static constexpr int kFlat = 4 * t + p;
+    static constexpr int kQ = (kFlat * kHalves + 4 * kSteps - 1) / (4 * kSteps);
+    static constexpr bool kUsed = kQ < kHalves && kQ * 4 * kSteps / kHalves == kFlat;
+};
+static_assert(kHalves <= 4 * kSteps, "more stash entries than MFMA slots");
+
+// Step t's operands: lanes 4h .. 4h + 3 of the thread's weight row and of
+// its two activation columns.
+__device__ __forceinline__ void read_step(const char *wl, const char *xl, int t, int h, int wrow, int xcol,
+                                          f32x4 &wa, f32x4 &x0, f32x4 &x1)
+{
+    wa = *reinterpret_cast<const f32x4 *>(wl + (2 * t + h) * kWG + wrow * 16);
+    x0 = *reinterpret_cast<const f32x4 *>(xl + (2 * t + h) * kXG + xcol * 16);
+    x1 = *reinterpret_cast<const f32x4 *>(xl + (2 * t + h) * kXG + (xcol + 32) * 16);
+}
+
+template <bool kBuf>
+__global__ __launch_bounds__(256) void tinyblas_mfma(GemmTable g, int64_t k, const uint16_t *__restrict__ a,
+                                                     int64_t n, int nct)
+{
+    __shared__ __attribute__((aligned(16))) char lds[2 * (kWBuf + kXBuf)];
+
+    int mi, rt, ct;
+    gemm_tile(g, xcd_tile(blockIdx.x, g.tile0[g.count]), nct, mi, rt, ct);
+    const int64_t rows = g.rows[mi];
+    float *__restrict__ out = g.out[mi];
+    const int64_t row0 = (int64_t)rt * kBM;
+    const int64_t col0 = (int64_t)ct * kBN;
+    const Src<kBuf> src(g.w[mi], rows, a, n, k, row0, col0);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int i = lane & 31;          // row (A) / column (B) within the 32 x 32 tile
+    const int h = lane >> 5;          // 0: chain lanes 0..3, 1: chain lanes 4..7
+    const int wrow = (wave >> 1) * 32 + i;  // the thread's weight row within the block
+    const int xcol = (wave & 1) * 64 + i;   // its first activation column within the block
+
+    f32x32 acc[2][4];
+#pragma unroll
+    for (int s = 0; s < 2; s++)
+#pragma unroll
+        for (int p = 0; p < 4; p++)
+#pragma unroll
+            for (int v = 0; v < 32; v++) acc[s][p][v] = 0.f;
+
+    // Pipeline: during stage st the MFMAs read LDS buffer st % 2, the chunks
+    // of stage st + 1 (in registers) are stashed into buffer (st + 1) % 2
+    // between them, and each register, once stashed, is reloaded with its
+    // chunk of stage st + 2, which so has a whole stage to arrive.  Chunks
+    // past k are zero, so the last stages need no special case.
+    const int64_t nstages = (k + kKS - 1) / kKS;
+    u32x4 wreg[kWPT], xreg[kXPT];
+    fetch_stage<kBuf>(wreg, xreg, src, 0, tid);
+    stash_stage(lds, lds + kWBuf, wreg, xreg, tid);
+    fetch_stage<kBuf>(wreg, xreg, src, kKS, tid);
+    __syncthreads();
+    for (int64_t st = 0; st < nstages; st++) {
+        const char *wl = lds + (st & 1) * (kWBuf + kXBuf);
+        const char *xl = wl + kWBuf;
+        char *nwl = lds + ((st + 1) & 1) * (kWBuf + kXBuf);
+        char *nxl = nwl + kWBuf;
+        const int64_t kfetch = (st + 2) * kKS;
+        // operands one step ahead of the MFMAs that use them
+        f32x4 wa, x0, x1;
+        read_step(wl, xl, 0, h, wrow, xcol, wa, x0, x1);
+        static_for<0, kSteps>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            f32x4 nwa, nx0, nx1;
+            if constexpr (t + 1 < kSteps) read_step(wl, xl, t + 1, h, wrow, xcol, nwa, nx0, nx1);
+            // keep the reads ahead of this step's MFMAs (their latency then
+            // hides behind the matrix core instead of stalling it)
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, 4>([&](auto pc) {
+                constexpr int p = decltype(pc)::value;
+                acc[0][p] = __builtin_amdgcn_mfma_f32_32x32x1f32(wa[p], x0[p], acc[0][p], 0, 0, 0);
+                acc[1][p] = __builtin_amdgcn_mfma_f32_32x32x1f32(wa[p], x1[p], acc[1][p], 0, 0, 0);
+                if constexpr (Slot<t, p>::kUsed) {
+                    constexpr int q = Slot<t, p>::kUsed ? Slot<t, p>::kQ : 0;
+                    __builtin_amdgcn_sched_barrier(0);
+                    stash_half<q>(nwl, nxl, wreg, xreg, tid);
+                    if constexpr (q % 2 == 1) fetch_chunk<kBuf, q / 2>(wreg, xreg, src, kfetch, tid);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            });
+            if constexpr (t + 1 < kSteps) {
+                wa = nwa;
+                x0 = nx0;
+                x1 = nx1;
+            }
+        });
+        // buffer (st + 1) % 2 is complete, and every wave is done reading
+        // buffer st % 2, which stage st + 1 overwrites
+        __syncthreads();
+    }
+
+    // hsum in the page's order, then out[c*rows + r] for 4 consecutive rows.
+    // Register v (< 16) of instruction p holds chain lane p and v + 16 lane
+    // p + 4 of the element at row (v / 4) * 8 + h * 4 + v % 4, column i.
+    const bool o16 = ((uintptr_t)out & 15) == 0;
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+        const int64_t c = col0 + xcol + 32 * s;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int64_t r = row0 + (wrow - i) + 8 * q + 4 * h;
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int v = 4 * q + e;
+                o[e] = ((acc[s][0][v] + acc[s][0][v + 16]) + (acc[s][2][v] + acc[s][2][v + 16])) +
+                       ((acc[s][1][v] + acc[s][1][v + 16]) + (acc[s][3][v] + acc[s][3][v + 16]));
+            }
+            // rows % 4 == 0 and r % 4 == 0: r < rows covers r .. r + 3
+            if (r < rows && c < n) {
+                float *dst = out + c * rows + r;
+                if (o16) {
+                    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+                } else {
+                    dst[0] = o[0];
+                    dst[1] = o[1];
+                    dst[2] = o[2];
+                    dst[3] = o[3];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_sgemm(GemmTable g, int64_t k, const uint16_t *a, int64_t n, bool aligned16,
+                        hipStream_t stream)
+{
+    const int64_t nct = (n + kBN - 1) / kBN;
+    int64_t tiles = 0;
+    for (int m = 0; m < g.count; m++) {
+        g.tile0[m] = (int32_t)tiles;
+        tiles += (g.rows[m] + kBM - 1) / kBM * nct;
+        if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
+    }
+    g.tile0[g.count] = (int32_t)tiles;
+    const dim3 grid((uint32_t)tiles);
+    // buffer offsets are 32-bit with bit 31 marking chunks past k: a tile of
+    // kBN columns must stay under 2^31 bytes
+    if (aligned16 && (int64_t)kBN * k * 2 < ((int64_t)1 << 31))
+        tinyblas_mfma<true><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+    else
+        tinyblas_mfma<false><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+    return hipGetLastError();
+}
+
+}  // namespace f16wm
