@@ -393,6 +393,35 @@ def test_large_magnitudes_and_cancellation(orc):
             assert_bits_equal(got.cpu().numpy(), orc.mat_mul(w, a[:nn]), "magnitudes k=%d n=%d" % (k, nn))
 
 
+def test_tinyblas_order_special_values(orc):
+    """The tinyBLAS order (computed one chain step per fp32 MFMA) on rows and
+    columns made of signed zeros, subnormals, the f16 extremes, infinities
+    and NaNs, over several output tiles with ragged edges; also an unaligned
+    activation pointer (the guarded-load kernel)."""
+    rows, k, n = 136, 264, 133
+    rng = np.random.default_rng(45)
+    w = synth.random_f16(61, (rows, k), 0.02)
+    a = synth.random_f16(62, (n, k))
+    w[0, :] = 0x8000                                    # -0 row
+    w[1, :] = rng.integers(1, 0x400, k)                 # positive subnormals
+    w[2, :] = rng.integers(0x8001, 0x8400, k)           # negative subnormals
+    w[3, ::2], w[3, 1::2] = 0x7BFF, 0xFBFF              # +-65504: cancellation at 2^32 scale
+    w[70, 9] = 0x7C00                                   # +inf in the second row tile
+    w[71, 17] = 0x7E00                                  # NaN
+    w[72, 3], w[72, 11] = 0x7C00, 0xFC00                # inf and -inf in one row: NaN
+    w[135, 263] = 0xFC00                                # -inf in the last row, last step
+    a[0, :] = 0x8000                                    # -0 column
+    a[1, :] = rng.integers(1, 0x400, k)                 # subnormal column
+    a[2, 5] = 0x7C00                                    # inf meets finite and zero weights
+    a[130, ::3] = 0x7BFF                                # a column in the ragged last tile
+    assert f16wm.takes_sgemm(rows, k, n)
+    want = orc.mat_mul(w, a)
+    got = f16wm.mat_mul(up16(w), up16(a))
+    assert_bits_equal(got.cpu().numpy(), want, "tinyBLAS specials")
+    got = f16wm.mat_mul(up16(w), up16(a, offset=1))
+    assert_bits_equal(got.cpu().numpy(), want, "tinyBLAS specials, unaligned activation")
+
+
 def test_repeatable_bits():
     w = up16(synth.random_f16(51, (1000, 4096), 0.02))
     a = up16(synth.random_f16(52, (7, 4096)))
