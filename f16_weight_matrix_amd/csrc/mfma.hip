@@ -16,14 +16,22 @@
 // Tiling: a 256-thread block computes BM columns x BN rows as 2 x 2 waves;
 // each wave owns (BM/2) x (BN/2) = TM x TN MFMA tiles of 32 x 32.  With
 // 128 x 128 per wave (16 tiles, 256 accumulators in AGPRs) every 16-byte LDS
-// fragment feeds four MFMAs, which keeps LDS reads at half the LDS bandwidth.
-// k is staged 32 at a time through two LDS buffers with 80-byte rows (a
-// stride that puts the 16 rows of one LDS read phase in 16 different bank
-// groups); the global loads of the next three stages are in flight during
-// the MFMAs (weights come from HBM with microseconds of latency).
-// Block b runs on XCD b % 8; tiles are handed out so each XCD walks a
-// contiguous range, and consecutive tiles share one weight-row block, so its
-// weights are read from HBM once and re-read from that XCD's L2.
+// fragment feeds four MFMAs.  Block b runs on XCD b % 8; tiles are handed out
+// so each XCD walks a contiguous range, and consecutive tiles share one
+// weight-row block, so its weights are read from HBM once and re-read from
+// that XCD's L2.
+//
+// Two kernels: mfma_fast (k % 64 == 0) stages k 64 at a time with direct
+// global-to-LDS loads (see there); mfma_generic (any k % 8 == 0) stages k 32
+// at a time through registers into LDS rows padded to 80 bytes (a stride that
+// puts the 16 rows of one LDS read phase in 16 different bank groups), with
+// the loads of the next three stages in flight.
+//
+// What bounds it: on this GPU the matrix cores alone, fed random f16
+// operands, sustain about 1.66 PFLOP/s (the clock drops to about 1.7 GHz at
+// the board's power limit); the 8B-shaped n = 512 products reach roughly
+// half of that, limited by keeping the operand stream from L2/HBM ahead of
+// the matrix cores.
 #include "kernels.h"
 
 namespace f16wm {
@@ -174,21 +182,38 @@ __global__ __launch_bounds__(256) void mfma_generic(GemmTable g, int64_t k, cons
         }
 }
 
-// Fast path: k % 64 == 0.  Same tiling and MFMA order as mfma_generic, with
-//  - buffer loads: each block addresses its activation and weight tiles
-//    through buffer resources whose size ends at the tile's last valid row,
-//    so rows past the matrix read as zero without a branch, and the prefetch
-//    running past the last stage reads zero (offset past the resource end);
-//  - 64-element k stages, two register sets (stages s+1 and s+2 in flight);
-//  - unpadded 128-byte LDS rows with the 16-byte chunk index XORed by
-//    (row / 2) % 8, which keeps both the row-wise stores and the 16-rows-per-
-//    phase fragment reads free of bank conflicts.
+// Fast path: k % 64 == 0.  Same MFMA and wave tiling as mfma_generic, fed
+// by direct global-to-LDS loads:
+//  - each operand tile is addressed through a buffer resource whose size
+//    ends at the tile's last valid row: rows past the matrix read as zero
+//    without a branch (their outputs are not stored);
+//  - buffer_load_dwordx4 with the lds bit writes a wave's 64 x 16 bytes to
+//    M0 + 16 * lane in LDS, with no trip through VGPRs and no ds_write: lane
+//    l of a load covers LDS row (l / 8) of its 8-row group and 16-byte slot
+//    l % 8, and fetches the global chunk that belongs in that slot, chunk =
+//    slot ^ ((row / 2) % 8).  That XOR swizzle keeps the 16-rows-per-phase
+//    fragment reads free of bank conflicts (128-byte LDS rows, unpadded);
+//  - k is staged 64 at a time through two LDS buffers: while stage s is
+//    multiplied, stage s + 1 is in flight; a wave waits for its own loads of
+//    stage s + 1 (vmcnt) and a plain s_barrier makes every wave's loads
+//    visible and frees the buffer the next loads overwrite.
+// Measured on this GPU against a register-staged version of the same tiling
+// (three stages in flight through VGPRs, ds_write into LDS): 5-15 % faster,
+// 72 instead of 186 VGPRs, no LDS data-FIFO stalls.
 constexpr int kFKS = 64;   // k per stage
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource over `bytes` from `base`.  Both are wave-uniform;
+// readfirstlane lets the compiler keep the descriptor in SGPRs.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base, int64_t bytes)
 {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    const int nb = __builtin_amdgcn_readfirstlane((int)bytes);
     // raw buffer: stride 0, num_records = bytes, gfx9 dword3
-    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, nb, 0x00020000);
 }
 
 template <int BM, int BN>
@@ -197,11 +222,10 @@ __global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const u
 {
     constexpr int WM = BM / 2, WN = BN / 2;       // wave tile
     constexpr int TM = WM / 32, TN = WN / 32;     // 32x32 MFMA tiles per wave
-    constexpr int AU = BM / 32;                   // activation units per thread per stage
-    constexpr int WU = BN / 32;                   // weight units per thread per stage
-    constexpr int ROWH = kFKS;                    // halves per LDS row (128 bytes)
-    constexpr int BUFH = (BM + BN) * ROWH;        // halves per LDS buffer
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUFH];
+    constexpr int ROWB = kFKS * 2;                // bytes per LDS row (8 chunks)
+    constexpr int STAGEB = (BM + BN) * ROWB;      // bytes per stage: [A rows | W rows]
+    constexpr int LA = BM / 32, LW = BN / 32;     // 8-row loads per wave per stage
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGEB];
 
     // XCD-aware tile index (blocks are dispatched round-robin over 8 XCDs),
     // then this tile's matrix.
@@ -215,26 +239,27 @@ __global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const u
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int lr = lane & 31;
     const int hi = lane >> 5;
 
-    // Tile resources (bytes of the valid rows of this tile).
     const int64_t arows = n - c0 < BM ? n - c0 : BM;
     const int64_t wrows = rows - r0 < BN ? rows - r0 : BN;
     const __amdgpu_buffer_rsrc_t ar = tile_rsrc(a + c0 * k, arows * k * 2);
     const __amdgpu_buffer_rsrc_t wr = tile_rsrc(w + r0 * k, wrows * k * 2);
-    // This thread's units: rows (tid >> 3) + 32 p, 16-byte chunk tid & 7.  All
-    // of a load's offset is in the VGPR offset, which the buffer range check
-    // covers; an offset at or past the resource size reads as zero.
-    const int urow = tid >> 3, uch = tid & 7;
-    const int voff = (int)(urow * k * 2 + uch * 16);
-    const int rstride = (int)(32 * k * 2);          // bytes between p and p + 1
-    const int past_end = 256 * (int)k * 2;          // >= every tile's resource size
+
+    // Load j < LA of this wave fills activation rows (wave * LA + j) * 8 .. +8
+    // of a stage, load LA + j weight rows (wave * LW + j) * 8 .. +8.  Byte
+    // offsets of stage 0; stage s adds 128 * s.
+    int voff[LA + LW];
+#pragma unroll
+    for (int j = 0; j < LA + LW; j++) {
+        const int trow = (j < LA ? wave * LA + j : wave * LW + j - LA) * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((trow >> 1) & 7);
+        voff[j] = (int)(trow * k * 2 + chunk * 16);
+    }
     const int64_t nstages = k / kFKS;
-    // LDS byte offsets of this thread's unit stores (row urow + 32 p, swizzled chunk)
-    const int st_off = urow * (ROWH * 2) + 16 * (uch ^ ((urow >> 1) & 7));
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -244,46 +269,40 @@ __global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const u
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-    u32x4 areg[2][AU], wreg[2][WU];
-    auto fetch = [&](int64_t s, int set) {
-        const bool live = s < nstages;
-        const int so = (int)(s * kFKS * 2);
+    // Stage s goes to LDS buffer s % 2.
+    auto issue = [&](int64_t s) {
+        unsigned char *buf = smem + (s & 1) * STAGEB;
+        const int so = (int)(s * ROWB);
 #pragma unroll
-        for (int p = 0; p < AU; p++)
-            areg[set][p] = __builtin_amdgcn_raw_buffer_load_b128(ar, live ? voff + p * rstride + so : past_end, 0, 0);
-#pragma unroll
-        for (int p = 0; p < WU; p++)
-            wreg[set][p] = __builtin_amdgcn_raw_buffer_load_b128(wr, live ? voff + p * rstride + so : past_end, 0, 0);
-    };
-    auto stash = [&](int set, int buf) {
-        unsigned char *base = reinterpret_cast<unsigned char *>(smem + buf * BUFH);
-#pragma unroll
-        for (int p = 0; p < AU; p++)
-            *reinterpret_cast<u32x4 *>(base + st_off + p * 32 * ROWH * 2) = areg[set][p];
-#pragma unroll
-        for (int p = 0; p < WU; p++)
-            *reinterpret_cast<u32x4 *>(base + BM * ROWH * 2 + st_off + p * 32 * ROWH * 2) = wreg[set][p];
+        for (int j = 0; j < LA + LW; j++) {
+            const int row0 = j < LA ? (wave * LA + j) * 8 : BM + (wave * LW + j - LA) * 8;
+            lds_void *dst = (lds_void *)(buf + row0 * ROWB);
+            const int off = voff[j] + so;
+            if (j < LA)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, off, 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, off, 0, 0, 0);
+        }
     };
     // Fragment rows of this lane: wm*WM + i*32 + lr (activations) and
-    // wn*WN + j*32 + lr (weights); all are lr modulo 16, so the swizzle is
-    // the same (lr >> 1) & 7 for every fragment.
+    // BM + wn*WN + j*32 + lr (weights); their swizzle is (lr >> 1) & 7.
     const int sw = (lr >> 1) & 7;
-    auto compute = [&](int buf) {
-        const unsigned char *base = reinterpret_cast<const unsigned char *>(smem + buf * BUFH);
-        const unsigned char *abase = base + (wm * WM + lr) * (ROWH * 2);
-        const unsigned char *wbase = base + BM * ROWH * 2 + (wn * WN + lr) * (ROWH * 2);
+    auto compute = [&](int64_t s) {
+        const unsigned char *base = smem + (s & 1) * STAGEB;
+        const unsigned char *abase = base + (wm * WM + lr) * ROWB;
+        const unsigned char *wbase = base + (BM + wn * WN + lr) * ROWB;
 #pragma unroll
         for (int kk = 0; kk < kFKS / 16; kk++) {
             const int ch = 16 * ((2 * kk + hi) ^ sw);
-            // let the scheduler interleave the fragment reads with the MFMAs
+            // let the scheduler interleave the next fragment reads with the MFMAs
             __builtin_amdgcn_iglp_opt(0);
             half8 af[TM], bf[TN];
 #pragma unroll
             for (int i = 0; i < TM; i++)
-                af[i] = *reinterpret_cast<const half8 *>(abase + i * 32 * ROWH * 2 + ch);
+                af[i] = *reinterpret_cast<const half8 *>(abase + i * 32 * ROWB + ch);
 #pragma unroll
             for (int j = 0; j < TN; j++)
-                bf[j] = *reinterpret_cast<const half8 *>(wbase + j * 32 * ROWH * 2 + ch);
+                bf[j] = *reinterpret_cast<const half8 *>(wbase + j * 32 * ROWB + ch);
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
@@ -292,20 +311,16 @@ __global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const u
         }
     };
 
-    // Stage s waits in register set s % 2 and is computed from LDS buffer s % 2.
-    fetch(0, 0);
-    fetch(1, 1);
-    stash(0, 0);
-    __syncthreads();
-    for (int64_t s = 0; s < nstages; s += 2) {
-        fetch(s + 2, 0);
-        compute(0);
-        stash(1, 1);
-        __syncthreads();
-        fetch(s + 3, 1);
-        compute(1);
-        stash(0, 0);
-        __syncthreads();
+    issue(0);
+    for (int64_t s = 0; s < nstages; s++) {
+        // This wave's loads of stage s are in LDS (vmcnt(0): only stage s was
+        // in flight); the barrier makes every wave's loads visible and
+        // guarantees stage s - 1 (the buffer the next loads fill) is done.
+        // A plain s_barrier: a compiler fence would add nothing here.
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt/lgkmcnt untouched
+        asm volatile("s_barrier" ::: "memory");
+        if (s + 1 < nstages) issue(s + 1);    // nothing is left in flight at the end
+        compute(s);
     }
 
 #pragma unroll
@@ -340,13 +355,17 @@ bool fill_tiles(GemmTable &g, int64_t n, int B, int64_t *nct_out)
 
 hipError_t launch_mfma(GemmTable g, int64_t k, const uint16_t *a, int64_t n, hipStream_t stream)
 {
-    // 256 x 256 tiles when they still give at least one block per CU,
-    // 128 x 128 otherwise.  The fast kernel needs k % 64 == 0 and 32-bit
-    // byte offsets inside one 256-row tile.
+    // Tile size, measured on the 8B-shaped products at n = 512: 256 x 256
+    // tiles (one block per CU, four waves) win only when their count fills
+    // one round of the 256 CUs nearly exactly (192..256 tiles, e.g. the
+    // grouped gate/up product); otherwise 128 x 128 tiles (two blocks per CU)
+    // are as fast or faster, and much faster when 256-tiles would leave CUs
+    // idle.  The fast kernel needs k % 64 == 0 and 32-bit byte offsets
+    // inside one 256-row tile.
     int64_t big = 0;
     for (int i = 0; i < g.count; i++) big += ((g.rows[i] + 255) / 256) * ((n + 255) / 256);
     const bool fast = k % kFKS == 0 && k > 0 && 256 * k * 2 < ((int64_t)1 << 31);
-    const int B = fast && big >= 256 ? 256 : 128;
+    const int B = fast && big >= 192 && big <= 256 ? 256 : 128;
     int64_t nct = 0;
     if (!fill_tiles(g, n, B, &nct)) return hipErrorInvalidConfiguration;
     const dim3 grid((uint32_t)g.tile0[g.count]);
