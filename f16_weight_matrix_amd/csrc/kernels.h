@@ -10,10 +10,14 @@ namespace f16wm {
 // Rows of up to F16WM_MAX_MULTI matrices that share k and one activation,
 // laid end to end: global row g belongs to matrix m when
 // row0[m] <= g < row0[m + 1].
+// tile0[m] is the first row tile of matrix m for kernels that give every
+// block the rows of one matrix only (filled by the launcher for its tile
+// height; tile0[count] is the tile total).
 struct RowTable {
     const uint16_t *w[F16WM_MAX_MULTI];
     float *out[F16WM_MAX_MULTI];
     int64_t row0[F16WM_MAX_MULTI + 1];
+    int64_t tile0[F16WM_MAX_MULTI + 1];
     int32_t count;
 };
 

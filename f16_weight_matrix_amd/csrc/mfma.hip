@@ -365,7 +365,7 @@ hipError_t launch_mfma(GemmTable g, int64_t k, const uint16_t *a, int64_t n, hip
     int64_t big = 0;
     for (int i = 0; i < g.count; i++) big += ((g.rows[i] + 255) / 256) * ((n + 255) / 256);
     const bool fast = k % kFKS == 0 && k > 0 && 256 * k * 2 < ((int64_t)1 << 31);
-    const int B = fast && big >= 192 && big <= 256 ? 256 : 128;
+    const int B = fast && big >= 192 ? 256 : 128;
     int64_t nct = 0;
     if (!fill_tiles(g, n, B, &nct)) return hipErrorInvalidConfiguration;
     const dim3 grid((uint32_t)g.tile0[g.count]);

@@ -173,62 +173,150 @@ struct LdsCfg {
     static_assert(R * U % 256 == 0, "whole units per thread");
 };
 
+// Buffer resource over `bytes` from `base` (both wave-uniform; readfirstlane
+// lets the compiler keep the descriptor in SGPRs).  An access at or past
+// `bytes` reads zero and touches no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    const int nb = __builtin_amdgcn_readfirstlane((int)bytes);
+    // raw buffer: stride 0, num_records = bytes, gfx9 dword3
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, nb, 0x00020000);
+}
+
+constexpr int kPastEnd = 0x7ffffff0;   // an offset past every resource: reads zero
+
+// Whole activation column in LDS when it is at most 32 KB of f16.
+constexpr int64_t kWholeMaxK = 16384;
+
+// Two f32 bit patterns rounded to f16 and packed (low element first).
+__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi)
+{
+    return (uint32_t)rne_f16(__uint_as_float(lo)) | ((uint32_t)rne_f16(__uint_as_float(hi)) << 16);
+}
+
+// Rounded f16 bit patterns of eight consecutive activation elements held as
+// raw data: two 16-byte halves of f32 values (kF32), or one of f16 patterns.
+// (Elements are copied out of the vectors before the bit cast: this clang
+// miscompiles __builtin_bit_cast applied to a vector element in place.)
+template <bool kF32>
+__device__ __forceinline__ u32x4 round8(const u32x4 (&r)[2])
+{
+    if (!kF32) return r[0];
+    const u32x4 p = r[0], q = r[1];
+    u32x4 o;
+    o[0] = pack2(p[0], p[1]);
+    o[1] = pack2(p[2], p[3]);
+    o[2] = pack2(q[0], q[1]);
+    o[3] = pack2(q[2], q[3]);
+    return o;
+}
+
 // kWhole: the whole activation column (k <= 16384 elements) is rounded or
-// copied into LDS once at the start, overlapping the first weight stage, and
+// copied into LDS once at the start, overlapping the first weight stages, and
 // the stages carry weights only; otherwise each stage also stages its SC
 // activation elements.  Dynamic LDS: 2 * (WBYTES, or BUFB) + (k * 2 if kWhole).
+//
+// Every block takes R rows of one matrix (row tile blockIdx.x - tile0[m] of
+// matrix m).  Weights and per-stage activations come through buffer loads
+// whose resources end at the tile's last row and the column's last element:
+// rows past the matrix, elements past k and stages past the last read zero
+// without a branch or any memory traffic, so every stage issues the same
+// loads and the compiler can wait for exactly the stage it needs.
+//
+// D register sets: the loads of stages s + 1 .. s + D are in flight while
+// stage s is multiplied (stage s + 1 waits in its registers until it is
+// copied into the other LDS buffer).  Matrices of a few thousand rows give
+// each CU only two or three blocks, so one stage in flight per block leaves
+// HBM latency exposed; D = 4 keeps 64 KB per block in flight.  Elements past
+// k inside a stage (the next row's, or zero) land in LDS positions the
+// multiply never reads: it stops at the last full 32-element step and the
+// k % 32 tail is read from global memory.
+//
+// The 64-row blocks (LPR = 4) serve only tall matrices with many blocks per
+// CU, where one stage in flight is enough; there the weights come through
+// plain non-temporal global loads, which measured 5 % faster than buffer
+// loads for the 128256 x 4096 logits GEMV (D = 1: the compiler waits for the
+// single stage, so the conditional loads cost nothing).
+template <int LPR>
+struct Depth {
+    static constexpr int D = LPR == 4 ? 1 : 4;
+    static constexpr bool kGlobal = LPR == 4;   // weights by global loads
+};
+
 template <int LPR, bool kF32, bool kWhole>
 __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const void *__restrict__ a_all)
 {
     typedef LdsCfg<LPR> C;
     typedef typename Halves<C::CPL>::T HT;
+    constexpr int D = Depth<LPR>::D;
     constexpr int BUF = kWhole ? C::WBYTES : C::BUFB;   // bytes per stage buffer
+    constexpr int ESZ = kF32 ? 4 : 2;                    // activation element bytes
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     unsigned char *actl = lds + 2 * BUF;                 // whole column (kWhole)
 
     const int tid = threadIdx.x;
     const int64_t col = blockIdx.y;
-    const void *a = static_cast<const char *>(a_all) + col * k * (kF32 ? 4 : 2);
-    const int64_t total = t.row0[t.count];
-    const int64_t g0 = (int64_t)blockIdx.x * C::R;
+    const void *a = static_cast<const char *>(a_all) + col * k * ESZ;
 
-    // Source rows of this thread's stage units (the same rows every stage).
-    const uint16_t *src[C::UPT];
+    // This block's matrix and row tile.
+    int m = 0;
+#pragma unroll
+    for (int i = 1; i < F16WM_MAX_MULTI; i++)
+        if (i < t.count && (int64_t)blockIdx.x >= t.tile0[i]) m = i;
+    const int64_t rows_m = t.row0[m + 1] - t.row0[m];
+    const int64_t r0 = ((int64_t)blockIdx.x - t.tile0[m]) * C::R;
+    const int64_t vrows = rows_m - r0 < C::R ? rows_m - r0 : C::R;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(t.w[m] + r0 * k, vrows * k * 2);
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(a, k * ESZ);
+
+    // Byte offsets of this thread's stage units in stage 0: unit f = row
+    // f / U, 16 bytes at element 8 * (f % U); stage s adds 2 * SC * s.
+    int woff[C::UPT];
 #pragma unroll
     for (int p = 0; p < C::UPT; p++) {
         const int f = p * 256 + tid;
-        const int64_t g = g0 + f / C::U;
-        src[p] = nullptr;
-        if (g < total) {
-            const int m = find_matrix(t, g);
-            src[p] = t.w[m] + (g - t.row0[m]) * k + 8 * (f % C::U);
-        }
+        woff[p] = (int)((f / C::U) * k * 2 + 16 * (f % C::U));
     }
     const bool act_loader = tid < C::U;
+    const int aoff = act_loader ? 8 * tid * ESZ : kPastEnd;
 
     const int64_t nsteps = k >> 5;                       // full 32-element steps
     const int64_t nstages = (k + C::SC - 1) / C::SC;
 
-    u32x4 wreg[C::UPT];
-    u32x4 areg;
-    auto fetch = [&](int64_t s) {
-        const int64_t k0 = s * C::SC;
+    u32x4 wreg[D][C::UPT];
+    u32x4 areg[D][2];
+    auto fetch = [&](int64_t s, int set) {
+        const bool live = s < nstages;
+        const int so = live ? (int)(s * C::SC * 2) : 0;
 #pragma unroll
         for (int p = 0; p < C::UPT; p++) {
-            const int f = p * 256 + tid;
-            if (src[p] && k0 + 8 * (f % C::U) < k)
-                wreg[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src[p] + k0));
+            if (Depth<LPR>::kGlobal) {
+                const int f = p * 256 + tid;
+                if (live && f / C::U < vrows && s * C::SC + 8 * (f % C::U) < k)
+                    wreg[set][p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                        t.w[m] + (r0 + f / C::U) * k + s * C::SC + 8 * (f % C::U)));
+            } else {
+                wreg[set][p] = __builtin_amdgcn_raw_buffer_load_b128(wr, live ? woff[p] + so : kPastEnd, 0, 2);
+            }
         }
-        if (!kWhole && act_loader && k0 + 8 * tid < k) areg = act8<kF32>(a, k0 + 8 * tid);
+        if (!kWhole) {
+            const int ao = live && act_loader ? aoff + (int)(s * C::SC * ESZ) : kPastEnd;
+            areg[set][0] = __builtin_amdgcn_raw_buffer_load_b128(ar, ao, 0, 0);
+            if (kF32) areg[set][1] = __builtin_amdgcn_raw_buffer_load_b128(ar, ao == kPastEnd ? ao : ao + 16, 0, 0);
+        }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int set, int buf) {
         unsigned char *base = lds + buf * BUF;
 #pragma unroll
         for (int p = 0; p < C::UPT; p++) {
             const int f = p * 256 + tid;
-            *reinterpret_cast<u32x4 *>(base + (f / C::U) * C::ROWB + 16 * (f % C::U)) = wreg[p];
+            *reinterpret_cast<u32x4 *>(base + (f / C::U) * C::ROWB + 16 * (f % C::U)) = wreg[set][p];
         }
-        if (!kWhole && act_loader) *reinterpret_cast<u32x4 *>(base + C::WBYTES + 16 * tid) = areg;
+        if (!kWhole && act_loader)
+            *reinterpret_cast<u32x4 *>(base + C::WBYTES + 16 * tid) = round8<kF32>(areg[set]);
     };
 
     const int rho = tid / LPR;
@@ -237,17 +325,8 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const 
 #pragma unroll
     for (int i = 0; i < C::CPL; i++) acc[i] = 0.f;
 
-    if (nstages > 0) fetch(0);
-    if (kWhole) {
-        // k % 8 == 0 here; visible to every thread after the barrier below
-        for (int64_t e = 8 * tid; e < k; e += 8 * 256)
-            *reinterpret_cast<u32x4 *>(actl + 2 * e) = act8<kF32>(a, e);
-    }
-    if (nstages > 0) stash(0);
-    __syncthreads();
-    for (int64_t s = 0; s < nstages; s++) {
+    auto compute = [&](int64_t s) {
         const int buf = (int)(s & 1);
-        if (s + 1 < nstages) fetch(s + 1);
         const unsigned char *wl = lds + buf * BUF + rho * C::ROWB + j * C::CPL * 2;
         const unsigned char *al = kWhole ? actl + 2 * s * C::SC + j * C::CPL * 2
                                          : lds + buf * C::BUFB + C::WBYTES + j * C::CPL * 2;
@@ -262,18 +341,59 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const 
                 fma_halves<C::CPL>(acc, *reinterpret_cast<const HT *>(wl + 64 * st),
                                    *reinterpret_cast<const HT *>(al + 64 * st));
         }
-        if (s + 1 < nstages) stash(buf ^ 1);
-        __syncthreads();
+    };
+
+    // Prologue.  The whole activation column (kWhole) is loaded first, 8
+    // elements per thread per round for every round a column of kWholeMaxK
+    // elements needs (rounds past k read zero and move no data), so the
+    // load count is the same for every k; then the first D weight stages.
+    // The column is written to LDS as soon as its own loads are in, while the
+    // weight stages are still in flight.
+    constexpr int NAR = kWhole ? (int)(kWholeMaxK / (8 * 256)) : 1;   // rounds
+    u32x4 araw[NAR][2];
+    if (kWhole) {
+#pragma unroll
+        for (int i = 0; i < NAR; i++) {
+            const int off = (tid + 256 * i) * 8 * ESZ;
+            araw[i][0] = __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0);
+            if (kF32) araw[i][1] = __builtin_amdgcn_raw_buffer_load_b128(ar, off + 16, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep them ahead of the weight loads
+    }
+#pragma unroll
+    for (int d = 0; d < D; d++) fetch(d, d);
+    if (kWhole) {
+        // k % 8 == 0 here; visible to every thread after the barrier below
+#pragma unroll
+        for (int i = 0; i < NAR; i++) {
+            const int64_t e = 8 * (tid + 256 * i);
+            if (e < k) *reinterpret_cast<u32x4 *>(actl + 2 * e) = round8<kF32>(araw[i]);
+        }
+    }
+    stash(0, 0);
+    __syncthreads();
+    // Stage s sits in LDS buffer s % 2 and came through register set s % D.
+    // The loop runs a whole number of D-stage rounds; the stages past the
+    // last only load zeros and skip the multiply, so every round issues the
+    // same loads.  Plain barriers: each wave's own LDS writes are complete
+    // (lgkmcnt(0)) before it arrives, and nothing else needs to drain.
+    const int64_t rounds = (nstages + D - 1) / D;
+    for (int64_t s0 = 0; s0 < rounds * D; s0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; d++) {
+            const int64_t s = s0 + d;
+            fetch(s + D, d);                     // set d is free: stage s is in LDS
+            if (s < nstages) compute(s);
+            stash((d + 1) % D, (int)((s + 1) & 1));
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
     }
 
     float v = vec_dot_tree<C::CPL>(acc);
-    const int64_t g = g0 + rho;
-    if (j == 0 && g < total) {
-        const int m = find_matrix(t, g);
-        const int64_t r = g - t.row0[m];
+    const int64_t r = r0 + rho;
+    if (j == 0 && r < rows_m) {
         const uint16_t *wrow = t.w[m] + r * k;
         if (k & 31) v = add_tail<kF32>(v, wrow, a, nsteps * 32, k);
-        const int64_t rows_m = t.row0[m + 1] - t.row0[m];
         t.out[m][col * rows_m + r] = v;
     }
 }
@@ -313,8 +433,6 @@ __global__ __launch_bounds__(256) void vec_dot_v1(RowTable t, int64_t k, const v
     }
 }
 
-// Whole activation column in LDS when it is at most 32 KB of f16.
-constexpr int64_t kWholeMaxK = 16384;
 
 // Allow a kernel the LDS it asks for beyond the default dynamic limit.
 template <typename K>
@@ -366,14 +484,25 @@ hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32a
         if (total >= 512 * 64) lpr = 4;
         else if (total >= 512 * 16) lpr = 16;
     }
+    // The LDS kernels address one row tile through 32-bit buffer offsets.
+    if (vec8 && (256 / 4) * k * 2 + 65536 > 0x7fff0000) vec8 = false;
     const int per = vec8 ? 256 / lpr : kV1Rows;
-    const int64_t bx = (total + per - 1) / per;
+    RowTable tt = t;
+    int64_t bx = (total + per - 1) / per;
+    if (vec8) {
+        bx = 0;
+        for (int i = 0; i < t.count; i++) {
+            tt.tile0[i] = bx;
+            bx += (t.row0[i + 1] - t.row0[i] + per - 1) / per;
+        }
+        tt.tile0[t.count] = bx;
+    }
     if (bx > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
     // grid.y is limited to 65535: launch column chunks, each with its own
     // activation and output offsets.
     for (int64_t c0 = 0; c0 < ncols; c0 += 65535) {
         const int64_t nc = ncols - c0 < 65535 ? ncols - c0 : 65535;
-        RowTable tc = t;
+        RowTable tc = tt;
         for (int i = 0; i < t.count; i++) tc.out[i] = t.out[i] + c0 * (t.row0[i + 1] - t.row0[i]);
         const dim3 grid((uint32_t)bx, (uint32_t)nc);
         const void *ac = static_cast<const char *>(a) + c0 * k * (f32act ? 4 : 2);
