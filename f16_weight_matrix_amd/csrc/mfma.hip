@@ -193,10 +193,14 @@ __global__ __launch_bounds__(256) void mfma_generic(GemmTable g, int64_t k, cons
 //    l % 8, and fetches the global chunk that belongs in that slot, chunk =
 //    slot ^ ((row / 2) % 8).  That XOR swizzle keeps the 16-rows-per-phase
 //    fragment reads free of bank conflicts (128-byte LDS rows, unpadded);
-//  - k is staged 64 at a time through two LDS buffers: while stage s is
-//    multiplied, stage s + 1 is in flight; a wave waits for its own loads of
-//    stage s + 1 (vmcnt) and a plain s_barrier makes every wave's loads
-//    visible and frees the buffer the next loads overwrite.
+//  - k is staged 64 at a time through NBUF LDS buffers: while stage s is
+//    multiplied, stages s + 1 .. s + NBUF - 1 are in flight; a wave waits
+//    for its own loads of stage s (vmcnt) and a plain s_barrier makes every
+//    wave's loads visible and frees the buffer the next loads overwrite.
+//    Launches with fewer 128 x 128 tiles than CUs (q/k/v, o, down at
+//    n = 512) are bound by that wait: one memory round trip per stage
+//    unless several stages are in flight, so they use NBUF = 4 (128 KB of
+//    LDS, one block per CU); the others use NBUF = 2.
 // Measured on this GPU against a register-staged version of the same tiling
 // (three stages in flight through VGPRs, ds_write into LDS): 5-15 % faster,
 // 72 instead of 186 VGPRs, no LDS data-FIFO stalls.
@@ -216,7 +220,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base
     return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, nb, 0x00020000);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NBUF>
 __global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const uint16_t *__restrict__ a,
                                                  int64_t n, int nct)
 {
@@ -225,7 +229,8 @@ __global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const u
     constexpr int ROWB = kFKS * 2;                // bytes per LDS row (8 chunks)
     constexpr int STAGEB = (BM + BN) * ROWB;      // bytes per stage: [A rows | W rows]
     constexpr int LA = BM / 32, LW = BN / 32;     // 8-row loads per wave per stage
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGEB];
+    constexpr int PAST_END = 0x7ffffff0;          // an offset past every tile: reads zero
+    __shared__ __attribute__((aligned(16))) unsigned char smem[NBUF * STAGEB];
 
     // XCD-aware tile index (blocks are dispatched round-robin over 8 XCDs),
     // then this tile's matrix.
@@ -269,15 +274,18 @@ __global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const u
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-    // Stage s goes to LDS buffer s % 2.
+    // Stage s goes to LDS buffer s % NBUF.  Every call issues the same loads
+    // (a stage past the last reads zero and moves no data), so the waits
+    // below can count them.
     auto issue = [&](int64_t s) {
-        unsigned char *buf = smem + (s & 1) * STAGEB;
+        unsigned char *buf = smem + (int)(s % NBUF) * STAGEB;
+        const bool live = s < nstages;
         const int so = (int)(s * ROWB);
 #pragma unroll
         for (int j = 0; j < LA + LW; j++) {
             const int row0 = j < LA ? (wave * LA + j) * 8 : BM + (wave * LW + j - LA) * 8;
             lds_void *dst = (lds_void *)(buf + row0 * ROWB);
-            const int off = voff[j] + so;
+            const int off = live ? voff[j] + so : PAST_END;
             if (j < LA)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, off, 0, 0, 0);
             else
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const u
     // BM + wn*WN + j*32 + lr (weights); their swizzle is (lr >> 1) & 7.
     const int sw = (lr >> 1) & 7;
     auto compute = [&](int64_t s) {
-        const unsigned char *base = smem + (s & 1) * STAGEB;
+        const unsigned char *base = smem + (int)(s % NBUF) * STAGEB;
         const unsigned char *abase = base + (wm * WM + lr) * ROWB;
         const unsigned char *wbase = base + (BM + wn * WN + lr) * ROWB;
 #pragma unroll
@@ -311,17 +319,25 @@ __global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const u
         }
     };
 
-    issue(0);
+    // vmcnt(N) with N = the loads of the NBUF - 2 younger stages; expcnt and
+    // lgkmcnt untouched (simm16: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+    // vmcnt[5:4] << 14).
+    constexpr int YOUNG = (NBUF - 2) * (LA + LW);
+    static_assert(YOUNG < 64, "vmcnt range");
+    constexpr int WAIT = (YOUNG & 15) | 0x0F70 | ((YOUNG >> 4) << 14);
+#pragma unroll
+    for (int s = 0; s < NBUF - 1; s++) issue(s);
     for (int64_t s = 0; s < nstages; s++) {
-        // This wave's loads of stage s are in LDS (vmcnt(0): only stage s was
-        // in flight); the barrier makes every wave's loads visible and
-        // guarantees stage s - 1 (the buffer the next loads fill) is done.
-        // A plain s_barrier: a compiler fence would add nothing here.
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt/lgkmcnt untouched
+        // This wave's loads of stage s are in LDS; the barrier makes every
+        // wave's loads visible and guarantees stage s - 1 (whose buffer the
+        // next loads fill) is done.  A plain s_barrier: a compiler fence
+        // would also wait for the younger stages.
+        __builtin_amdgcn_s_waitcnt(WAIT);
         asm volatile("s_barrier" ::: "memory");
-        if (s + 1 < nstages) issue(s + 1);    // nothing is left in flight at the end
+        issue(s + NBUF - 1);
         compute(s);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // the zero loads past the end have landed
 
 #pragma unroll
     for (int i = 0; i < TM; i++)
@@ -356,25 +372,28 @@ bool fill_tiles(GemmTable &g, int64_t n, int B, int64_t *nct_out)
 hipError_t launch_mfma(GemmTable g, int64_t k, const uint16_t *a, int64_t n, hipStream_t stream)
 {
     // Tile size, measured on the 8B-shaped products at n = 512: 256 x 256
-    // tiles (one block per CU, four waves) win only when their count fills
-    // one round of the 256 CUs nearly exactly (192..256 tiles, e.g. the
-    // grouped gate/up product); otherwise 128 x 128 tiles (two blocks per CU)
-    // are as fast or faster, and much faster when 256-tiles would leave CUs
-    // idle.  The fast kernel needs k % 64 == 0 and 32-bit byte offsets
-    // inside one 256-row tile.
+    // tiles (one block per CU, four waves) once there are at least 192 of
+    // them (the logits and the grouped gate/up product); 128 x 128 tiles (two
+    // blocks per CU) below that, where 256-tiles would leave CUs idle, with
+    // four LDS stages when even the 128-tiles are fewer than the CUs (q/k/v,
+    // o, down).  The fast kernel needs
+    // k % 64 == 0 and 32-bit byte offsets inside one 256-row tile.
     int64_t big = 0;
     for (int i = 0; i < g.count; i++) big += ((g.rows[i] + 255) / 256) * ((n + 255) / 256);
     const bool fast = k % kFKS == 0 && k > 0 && 256 * k * 2 < ((int64_t)1 << 31);
     const int B = fast && big >= 192 ? 256 : 128;
     int64_t nct = 0;
     if (!fill_tiles(g, n, B, &nct)) return hipErrorInvalidConfiguration;
-    const dim3 grid((uint32_t)g.tile0[g.count]);
+    const int64_t tiles = g.tile0[g.count];
+    const dim3 grid((uint32_t)tiles);
     if (!fast)
         mfma_generic<128, 128><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
     else if (B == 256)
-        mfma_fast<256, 256><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+        mfma_fast<256, 256, 2><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+    else if (tiles < 256)   // fewer tiles than CUs: more stages in flight per tile
+        mfma_fast<128, 128, 4><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
     else
-        mfma_fast<128, 128><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+        mfma_fast<128, 128, 2><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
     return hipGetLastError();
 }
 
