@@ -233,11 +233,19 @@ def main():
     gemv_ms = [[a.elapsed_time(b) for a, b in ge] for ge in gemv_ms]
 
     # Roofline of the kernel `value` is about: vec_dot_lds<4>, the logits GEMV
-    # (70 % of the decode bytes); average duration of its launches, measured
-    # with HIP events on the stream the library launches on (torch's current).
-    n_gemv = len(gemv_launches)
+    # (70 % of the decode bytes); average duration of its launches: K of them
+    # back to back between two HIP events on the stream the library launches
+    # on (torch's current), so the events' own cost is spread over K launches.
+    # Each launch streams the 1.05 GB matrix, four times the last-level cache,
+    # so none of them finds its weights cached.
     li = [name for name, _, _ in gemv_launches].index("logits")
-    logits_ms = sum(r[li] for r in gemv_ms) / K
+    ev0, ev1 = ev(), ev()
+    ev0.record()
+    for _ in range(K):
+        f16wm.mat_vec(W["logits"], X1["logits"], O1["logits"])
+    ev1.record()
+    torch.cuda.synchronize()
+    logits_ms = ev0.elapsed_time(ev1) / K
     achieved = gemv_b[li] / (logits_ms * 1e-3) / 1e9
     per_launch = {name: {"bytes": gemv_b[i], "avg_us": round(1e3 * sum(r[i] for r in gemv_ms) / K, 2),
                          "GB_s": round(gemv_b[i] / (sum(r[i] for r in gemv_ms) / K * 1e-3) / 1e9, 1)}
