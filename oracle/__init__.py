@@ -62,6 +62,10 @@ class Oracle:
         L.oracle_exact_dot.argtypes = [P, P, I64, P]
         L.oracle_exact_dot.restype = ctypes.c_double
         L.oracle_fp64_at.argtypes = [P, I64, P, P, P, I64, P, P]
+        L.oracle_mat_mul_out.argtypes = [P, I64, I64, P, I64, ctypes.c_int, P, ctypes.c_int]
+        L.oracle_kq.argtypes = [P, I64, I64, I64, P, I64, P]
+        L.oracle_mad.argtypes = [P, P, P, I64, I64]
+        L.oracle_scale.argtypes = [P, P, I64, I64]
         self.L = L
 
     def to_f16(self, x) -> np.ndarray:
@@ -154,6 +158,58 @@ class Oracle:
         self.L.oracle_fp64_at(_p(w), k, _p(a), _p(rr), _p(cc), rr.size, _p(ref), _p(scale))
         return ref, scale
 
+    # the last layer's output columns (forward page, "Why only the output rows
+    # leave the last layer")
+    OUT_NONE, OUT_LAST, OUT_ALL = 0, 1, 2
+
+    def mat_mul_out(self, w, a, mode: int, threads: int = 0):
+        """The product over the output columns only: mode OUT_NONE -> None,
+        OUT_LAST -> out [rows] of the last column (vec_dot), OUT_ALL -> out
+        [n][rows] (order by takes_sgemm(rows, k, n))."""
+        w, a = _u16(w), _u16(a)
+        if a.ndim == 1:
+            a = a.reshape(1, -1)
+        rows, k = w.shape
+        n = a.shape[0]
+        assert a.shape[1] == k and mode in (0, 1, 2)
+        if mode == 0:
+            return None
+        out = np.empty((rows,) if mode == 1 else (n, rows), dtype=np.float32)
+        self.L.oracle_mat_mul_out(_p(w), rows, k, _p(a), n, mode, _p(out), threads)
+        return out
+
+    def kq(self, kc, q):
+        """Scores of queries q [n_head][d] against an f16 K cache kc
+        [n_kv][n_kv_head][d]: out [n_head][n_kv], vec_dot order."""
+        kc, q = _u16(kc), _u16(q)
+        n_kv, n_kv_head, d = kc.shape
+        n_head = q.shape[0]
+        assert q.shape == (n_head, d) and n_head % n_kv_head == 0
+        out = np.empty((n_head, n_kv), dtype=np.float32)
+        self.L.oracle_kq(_p(kc), n_kv, n_kv_head, d, _p(q), n_head, _p(out))
+        return out
+
+    def mad(self, acc, v, w):
+        """acc [nvec][n] f16 updated in a copy: to_f16(fma(v, w[b], acc))."""
+        acc = _u16(acc).copy()
+        v = _u16(v)
+        if acc.ndim == 1:
+            acc, v = acc.reshape(1, -1), v.reshape(1, -1)
+        w = np.ascontiguousarray(np.atleast_1d(w), dtype=np.float32)
+        assert acc.shape == v.shape and w.shape == (acc.shape[0],)
+        self.L.oracle_mad(_p(acc), _p(v), _p(w), acc.shape[0], acc.shape[1])
+        return acc
+
+    def scale(self, acc, s):
+        """acc [nvec][n] f16 scaled in a copy: to_f16(acc * s[b])."""
+        acc = _u16(acc).copy()
+        if acc.ndim == 1:
+            acc = acc.reshape(1, -1)
+        s = np.ascontiguousarray(np.atleast_1d(s), dtype=np.float32)
+        assert s.shape == (acc.shape[0],)
+        self.L.oracle_scale(_p(acc), _p(s), acc.shape[0], acc.shape[1])
+        return acc
+
 
 def _p(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
@@ -182,6 +238,6 @@ def default() -> Oracle:
 def __getattr__(name):
     # module-level access (oracle.vec_dot, ...) goes to the default build
     if name in ("to_f16", "widen", "vec_dot", "sgemm_dot", "takes_sgemm", "mat_mul", "mat_vec",
-                "mat_vec_multi", "mat_mul_at", "exact_dot", "fp64_at"):
+                "mat_vec_multi", "mat_mul_at", "exact_dot", "fp64_at", "mat_mul_out", "kq", "mad", "scale"):
         return getattr(default(), name)
     raise AttributeError(name)

@@ -330,3 +330,80 @@ void oracle_fp64_at(const uint16_t *w, int64_t k, const uint16_t *a,
         scale[i] = sa;
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* The last layer's output columns (forward page)                       */
+/* ------------------------------------------------------------------ */
+
+/*
+ * mat_mul_out: bankML page "bankML/forward.rs", section "Why only the output
+ * rows leave the last layer": on the last layer of a prompt only the rows
+ * llama.cpp outputs (its inp_out_ids: none, the last, or all) go through the
+ * feed-forward block, and for F16 weights the number of those rows decides
+ * the float order (one column: vec_dot; two or more: tinyBLAS when
+ * takes_sgemm holds).  mode 0 = none (nothing written), 1 = the last column
+ * (out: rows f32), 2 = all n columns (out: n x rows f32).
+ */
+void oracle_mat_mul_out(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
+                        int mode, float *out, int nthreads)
+{
+    if (mode == 1 && n >= 1) oracle_mat_mul(w, rows, k, a + (n - 1) * k, 1, out, nthreads);
+    else if (mode == 2) oracle_mat_mul(w, rows, k, a, n, out, nthreads);
+}
+
+/* ------------------------------------------------------------------ */
+/* The attention helpers over an f16 KV cache (f16 page)                */
+/* ------------------------------------------------------------------ */
+
+/*
+ * kq: attention scores against an f16 K cache.  f16 page, Technical usage:
+ * vec_dot_u16 is vec_dot with the first operand given as f16 values (a K
+ * cache row); Summary: the attention code uses it for K-cache rows.  Cache
+ * layout per layer: kc[p][j][0..d) for position p < n_kv and KV head
+ * j < n_kv_head (position-major, as llama.cpp stores a layer's K); query
+ * head h uses KV head h / (n_head / n_kv_head) (grouped-query attention).
+ * out[h * n_kv + p] = vec_dot(kc[p][h / G], q[h]), q: n_head x d f16.
+ */
+void oracle_kq(const uint16_t *kc, int64_t n_kv, int64_t n_kv_head, int64_t d, const uint16_t *q,
+               int64_t n_head, float *out)
+{
+    const int64_t G = n_head / n_kv_head;
+    for (int64_t h = 0; h < n_head; h++)
+        for (int64_t p = 0; p < n_kv; p++)
+            out[h * n_kv + p] = oracle_vec_dot(kc + (p * n_kv_head + h / G) * d, q + h * d, d);
+}
+
+/*
+ * mad: ggml_vec_mad_f16, the flash-attention V accumulator (f16 page,
+ * Technical usage `mad(acc, v, w)`; How it is verified: checked against the
+ * scalar definition, odd tails included).  The page names the function but
+ * not its arithmetic; our reading (parity partly unpinned): every element is
+ * acc[i] = to_f16(fma(widen(v[i]), w, widen(acc[i]))), one fused multiply-add
+ * in f32 (the F16C + FMA vector body; the scalar tail contracts to the same
+ * FMA), then rounded to f16.  Here for nvec vectors of n elements with one
+ * weight per vector: acc[b][i] with w[b].
+ */
+void oracle_mad(uint16_t *acc, const uint16_t *v, const float *w, int64_t nvec, int64_t n)
+{
+    need_widen();
+    for (int64_t b = 0; b < nvec; b++)
+        for (int64_t i = 0; i < n; i++) {
+            const int64_t e = b * n + i;
+            acc[e] = oracle_to_f16_one(fmaf(W16(v[e]), w[b], W16(acc[e])));
+        }
+}
+
+/*
+ * scale: ggml_vec_scale_f16 (f16 page, Technical usage `scale(acc, s)`):
+ * acc[i] = to_f16(widen(acc[i]) * s), one f32 multiply, then rounded to f16.
+ * For nvec vectors of n elements with one factor per vector: acc[b][i], s[b].
+ */
+void oracle_scale(uint16_t *acc, const float *s, int64_t nvec, int64_t n)
+{
+    need_widen();
+    for (int64_t b = 0; b < nvec; b++)
+        for (int64_t i = 0; i < n; i++) {
+            const int64_t e = b * n + i;
+            acc[e] = oracle_to_f16_one(W16(acc[e]) * s[b]);
+        }
+}

@@ -5,7 +5,9 @@ Every mutant below is a one-line slip someone could make while writing the
 orders from the bankML f16 page (Design notes): a wrong pairing at any level
 of either tree, the tail summed in f32, a mis-indexed chain, a dropped tail
 term, the wrong path rule, a transposed output, a rounding slip in to_f16 or
-widen.  The test builds each copy, binds the oracle's API to it and runs the
+widen; and in the next rows: the wrong output column of the last layer, a
+K-cache layout or head-mapping slip, an unfused or mis-indexed mad, a
+mis-indexed scale.  The test builds each copy, binds the oracle's API to it and runs the
 pin functions from test_oracle_orders / test_oracle_convert against it.
 """
 import inspect
@@ -16,6 +18,7 @@ import pytest
 
 import oracle
 import test_oracle_convert as tc
+import test_oracle_next as tn
 import test_oracle_orders as to
 
 SRC = open(os.path.join(os.path.dirname(oracle.__file__), "f16wm_oracle.c")).read()
@@ -70,12 +73,25 @@ MUTANTS = {
         "ldexpf((float)f, -24)", "ldexpf((float)f, -25)"),
     "widen normal bias": (
         "ldexpf((float)(1024u + f), (int)e - 25)", "ldexpf((float)(1024u + f), (int)e - 24)"),
+    "mat_mul_out takes the first column": (
+        "a + (n - 1) * k, 1, out, nthreads);", "a, 1, out, nthreads);"),
+    "kq maps query heads round-robin": (
+        "(p * n_kv_head + h / G) * d", "(p * n_kv_head + h % n_kv_head) * d"),
+    "kq reads a head-major cache": (
+        "(p * n_kv_head + h / G) * d", "(h / G * n_kv + p) * d"),
+    "mad rounds the product first": (
+        "oracle_to_f16_one(fmaf(W16(v[e]), w[b], W16(acc[e])))",
+        "oracle_to_f16_one(W16(v[e]) * w[b] + W16(acc[e]))"),
+    "mad uses the first vector's weight": (
+        "fmaf(W16(v[e]), w[b], W16(acc[e]))", "fmaf(W16(v[e]), w[0], W16(acc[e]))"),
+    "scale uses the first vector's factor": (
+        "oracle_to_f16_one(W16(acc[e]) * s[b])", "oracle_to_f16_one(W16(acc[e]) * s[0])"),
 }
 
 
 def _pins():
     fns = []
-    for mod in (to, tc):
+    for mod in (to, tc, tn):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
             if not name.startswith("test_") or fn.__module__ != mod.__name__:
                 continue
@@ -90,8 +106,11 @@ def _params(fn):
     marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
     if not marks:
         return [{}]
-    argname, values = marks[0].args
-    return [{argname: v} for v in values]
+    argnames, values = marks[0].args
+    names = [a.strip() for a in argnames.split(",")] if isinstance(argnames, str) else list(argnames)
+    if len(names) == 1:
+        return [{names[0]: v} for v in values]
+    return [dict(zip(names, v)) for v in values]
 
 
 def _fails(orc, fn):
