@@ -64,9 +64,14 @@ def lib() -> ctypes.CDLL:
         L.f16wm_mat_mul_multi.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, I64, P]
         L.f16wm_mat_mul_mfma_multi.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, I64, P]
         L.f16wm_takes_sgemm.argtypes = [I64, I64, I64]
+        L.f16wm_mat_mul_out.argtypes = [P, I64, I64, P, I64, I32, P, P]
+        L.f16wm_kq.argtypes = [P, I64, I64, I64, P, I64, P, P]
+        L.f16wm_mad.argtypes = [P, P, P, I64, I64, P]
+        L.f16wm_scale.argtypes = [P, P, I64, I64, P]
         for f in ("f16wm_to_f16", "f16wm_widen", "f16wm_get_rows", "f16wm_mat_vec", "f16wm_mat_vec_multi", "f16wm_mat_vec_f32",
                   "f16wm_mat_vec_multi_f32", "f16wm_mat_mul", "f16wm_mat_mul_mfma", "f16wm_mat_mul_multi",
-                  "f16wm_mat_mul_mfma_multi", "f16wm_takes_sgemm"):
+                  "f16wm_mat_mul_mfma_multi", "f16wm_takes_sgemm", "f16wm_mat_mul_out", "f16wm_kq", "f16wm_mad",
+                  "f16wm_scale"):
             getattr(L, f).restype = ctypes.c_int
         L.f16wm_last_error.restype = ctypes.c_char_p
         L.f16wm_last_error.argtypes = []
@@ -313,3 +318,91 @@ def mat_mul_multi(ws, a: torch.Tensor, outs=None) -> list:
 def mat_mul_mfma_multi(ws, a: torch.Tensor, outs=None) -> list:
     """The MFMA products of several matrices (same k) with one activation block, one launch."""
     return _mm_multi(lib().f16wm_mat_mul_mfma_multi, ws, a, outs)
+
+
+# Which columns of a micro-batch leave the last layer (mat_mul_out).
+OUT_NONE, OUT_LAST, OUT_ALL = 0, 1, 2
+
+
+def mat_mul_out(w: torch.Tensor, a: torch.Tensor, mode: int, out: torch.Tensor | None = None):
+    """The last layer's product over the columns that leave the model: mode
+    OUT_NONE -> None, OUT_LAST -> [rows] (the last column alone: vec_dot),
+    OUT_ALL -> [n, rows] (mat_mul)."""
+    rows, k = _wk(w)
+    _f16(a, "a")
+    if a.dim() == 1:
+        a = a.view(1, -1)
+    if a.dim() != 2 or a.shape[1] != k:
+        raise ValueError("a must be [n, k] with k = %d" % k)
+    n = a.shape[0]
+    if mode not in (OUT_NONE, OUT_LAST, OUT_ALL):
+        raise ValueError("mode must be OUT_NONE, OUT_LAST or OUT_ALL")
+    if mode == OUT_NONE:
+        with torch.cuda.device(w.device):
+            _check(lib().f16wm_mat_mul_out(w.data_ptr(), rows, k, a.data_ptr(), n, mode, None,
+                                           _stream(w.device)))
+        return None
+    m = 1 if mode == OUT_LAST else n
+    if out is None:
+        out = torch.empty((rows,) if mode == OUT_LAST else (n, rows), dtype=torch.float32, device=w.device)
+    _f32(out, "out")
+    if out.numel() != m * rows:
+        raise ValueError("out must have %d elements" % (m * rows))
+    with torch.cuda.device(w.device):
+        _check(lib().f16wm_mat_mul_out(w.data_ptr(), rows, k, a.data_ptr(), n, mode, out.data_ptr(),
+                                       _stream(w.device)))
+    return out
+
+
+def kq(kc: torch.Tensor, q: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """vec_dot scores of queries q [n_head, d] against an f16 K cache kc
+    [n_kv, n_kv_head, d] (grouped-query heads): [n_head, n_kv] f32."""
+    _f16(kc, "kc")
+    _f16(q, "q")
+    if kc.dim() != 3 or q.dim() != 2 or q.shape[1] != kc.shape[2]:
+        raise ValueError("kc must be [n_kv, n_kv_head, d] and q [n_head, d]")
+    n_kv, n_kv_head, d = kc.shape
+    n_head = q.shape[0]
+    if out is None:
+        out = torch.empty((n_head, n_kv), dtype=torch.float32, device=kc.device)
+    _f32(out, "out")
+    if out.numel() != n_head * n_kv:
+        raise ValueError("out must have n_head*n_kv elements")
+    with torch.cuda.device(kc.device):
+        _check(lib().f16wm_kq(kc.data_ptr(), n_kv, n_kv_head, d, q.data_ptr(), n_head, out.data_ptr(),
+                              _stream(kc.device)))
+    return out
+
+
+def _vecs(acc: torch.Tensor, f: torch.Tensor, fname: str):
+    _f16(acc, "acc")
+    if acc.dim() == 1:
+        nvec, n = 1, acc.shape[0]
+    elif acc.dim() == 2:
+        nvec, n = acc.shape
+    else:
+        raise ValueError("acc must be [n] or [nvec, n]")
+    _f32(f, fname)
+    if f.numel() != nvec:
+        raise ValueError("%s must have one value per vector (%d)" % (fname, nvec))
+    return nvec, n
+
+
+def mad(acc: torch.Tensor, v: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """In place: acc[b] = f16(fma(v[b], w[b], acc[b])) for f16 acc, v [nvec, n]
+    and f32 weights w [nvec] (all on the GPU).  Returns acc."""
+    nvec, n = _vecs(acc, w, "w")
+    _f16(v, "v")
+    if v.numel() != acc.numel():
+        raise ValueError("v must match acc")
+    with torch.cuda.device(acc.device):
+        _check(lib().f16wm_mad(acc.data_ptr(), v.data_ptr(), w.data_ptr(), nvec, n, _stream(acc.device)))
+    return acc
+
+
+def scale(acc: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
+    """In place: acc[b] = f16(acc[b] * s[b]) for f16 acc [nvec, n] and f32 s [nvec]."""
+    nvec, n = _vecs(acc, s, "s")
+    with torch.cuda.device(acc.device):
+        _check(lib().f16wm_scale(acc.data_ptr(), s.data_ptr(), nvec, n, _stream(acc.device)))
+    return acc

@@ -367,4 +367,82 @@ int f16wm_mat_mul_mfma_multi(const f16wm_mat *mats, int32_t count, int64_t k, co
     return mat_mul_impl("f16wm_mat_mul_mfma_multi", mats, count, k, a, n, true, stream);
 }
 
+int f16wm_mat_mul_out(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n, int32_t mode,
+                      float *out, void *stream)
+{
+    const char *fn = "f16wm_mat_mul_out";
+    if (mode != F16WM_OUT_NONE && mode != F16WM_OUT_LAST && mode != F16WM_OUT_ALL)
+        return fail(F16WM_EINVAL, "%s: mode %d is not none (0), last (1) or all (2)", fn, (int)mode);
+    if (rows < 0 || k < 0 || n < 0)
+        return fail(F16WM_EINVAL, "%s: negative size (rows=%lld k=%lld n=%lld)", fn, (long long)rows,
+                    (long long)k, (long long)n);
+    if (mode == F16WM_OUT_NONE) return ok();
+    if (mode == F16WM_OUT_ALL) {
+        const f16wm_mat m = {w, rows, out};
+        return mat_mul_impl(fn, &m, 1, k, a, n, false, stream);
+    }
+    if (n < 1) return fail(F16WM_EINVAL, "%s: the last column of an empty micro-batch", fn);
+    int64_t off;
+    if (!mul_ok(n - 1, k, &off)) return fail(F16WM_EINVAL, "%s: size too large", fn);
+    if (k > 0 && !a) return fail(F16WM_EINVAL, "%s: null activation", fn);
+    // one column: the vec_dot order of f16wm_mat_vec
+    return mat_vec_impl(fn, w, rows, k, a ? a + off : a, false, out, stream);
+}
+
+int f16wm_kq(const uint16_t *kc, int64_t n_kv, int64_t n_kv_head, int64_t d, const uint16_t *q, int64_t n_head,
+             float *out, void *stream)
+{
+    const char *fn = "f16wm_kq";
+    if (n_kv < 0 || n_kv_head < 0 || d < 0 || n_head < 0)
+        return fail(F16WM_EINVAL, "%s: negative size", fn);
+    if (n_kv_head == 0 || n_head % n_kv_head != 0)
+        return fail(F16WM_EINVAL, "%s: n_head (%lld) must be a multiple of n_kv_head (%lld) > 0", fn,
+                    (long long)n_head, (long long)n_kv_head);
+    if (n_kv_head > 65535) return fail(F16WM_EUNSUPPORTED, "%s: more than 65535 KV heads", fn);
+    int64_t rows, ke, qe, oe;
+    if (!mul_ok(n_kv, n_kv_head, &rows) || !mul_ok(rows, d, &ke) || !mul_ok(n_head, d, &qe) ||
+        !mul_ok(n_head, n_kv, &oe))
+        return fail(F16WM_EINVAL, "%s: size too large", fn);
+    if ((ke > 0 && !kc) || (qe > 0 && !q) || (oe > 0 && !out))
+        return fail(F16WM_EINVAL, "%s: null pointer for a non-empty array", fn);
+    if (!aligned(kc, 2) || !aligned(q, 2) || !aligned(out, 4))
+        return fail(F16WM_EINVAL, "%s: misaligned pointer", fn);
+    const Span so = span(out, oe * 4);
+    if (overlap(so, span(kc, ke * 2)) || overlap(so, span(q, qe * 2)))
+        return fail(F16WM_EINVAL, "%s: output overlaps an input", fn);
+    if (oe == 0) return ok();
+    if (int rc = check_device(fn)) return rc;
+    const bool vec8 = d % 8 == 0 && aligned(kc, 16) && aligned(q, 16);
+    return launched(fn, f16wm::launch_kq(kc, n_kv, n_kv_head, d, q, n_head, vec8, out, (hipStream_t)stream));
+}
+
+int f16wm_mad(uint16_t *acc, const uint16_t *v, const float *w, int64_t nvec, int64_t n, void *stream)
+{
+    const char *fn = "f16wm_mad";
+    int64_t e;
+    if (nvec < 0 || n < 0 || !mul_ok(nvec, n, &e)) return fail(F16WM_EINVAL, "%s: bad size", fn);
+    if (e == 0) return ok();
+    if (!acc || !v || !w) return fail(F16WM_EINVAL, "%s: null pointer", fn);
+    if (!aligned(acc, 2) || !aligned(v, 2) || !aligned(w, 4)) return fail(F16WM_EINVAL, "%s: misaligned pointer", fn);
+    if (overlap(span(acc, e * 2), span(v, e * 2)) || overlap(span(acc, e * 2), span(w, nvec * 4)))
+        return fail(F16WM_EINVAL, "%s: acc overlaps an input", fn);
+    if (int rc = check_device(fn)) return rc;
+    const bool vec8 = n % 8 == 0 && aligned(acc, 16) && aligned(v, 16);
+    return launched(fn, f16wm::launch_mad(acc, v, w, nvec, n, vec8, (hipStream_t)stream));
+}
+
+int f16wm_scale(uint16_t *acc, const float *s, int64_t nvec, int64_t n, void *stream)
+{
+    const char *fn = "f16wm_scale";
+    int64_t e;
+    if (nvec < 0 || n < 0 || !mul_ok(nvec, n, &e)) return fail(F16WM_EINVAL, "%s: bad size", fn);
+    if (e == 0) return ok();
+    if (!acc || !s) return fail(F16WM_EINVAL, "%s: null pointer", fn);
+    if (!aligned(acc, 2) || !aligned(s, 4)) return fail(F16WM_EINVAL, "%s: misaligned pointer", fn);
+    if (overlap(span(acc, e * 2), span(s, nvec * 4))) return fail(F16WM_EINVAL, "%s: acc overlaps s", fn);
+    if (int rc = check_device(fn)) return rc;
+    const bool vec8 = n % 8 == 0 && aligned(acc, 16);
+    return launched(fn, f16wm::launch_scale(acc, s, nvec, n, vec8, (hipStream_t)stream));
+}
+
 }  // extern "C"

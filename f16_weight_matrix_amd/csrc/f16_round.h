@@ -20,4 +20,15 @@ __device__ __forceinline__ uint16_t rne_f16(float x)
     return h;
 }
 
+// The same rounding of an f32 value the kernel has just computed (a product
+// or an FMA).  The empty asm makes the value opaque, so the compiler cannot
+// fuse the operation that produced it with the conversion: it would emit
+// v_fma_mixlo_f16 / v_mad_mixlo_f16, one rounding from the exact result
+// straight to f16, which differs from rounding to f32 first at f16 ties.
+__device__ __forceinline__ uint16_t rne_f16_of_result(float x)
+{
+    asm("" : "+v"(x));
+    return rne_f16(x);
+}
+
 }  // namespace f16wm

@@ -76,6 +76,17 @@ hipError_t launch_widen(const uint16_t *h, float *y, int64_t count, hipStream_t 
 hipError_t launch_get_rows(const uint16_t *w, int64_t rows, int64_t k, const int64_t *ids, int64_t nids,
                            float *out, hipStream_t stream);
 
+// vec_dot scores of n_head queries against an f16 K cache [n_kv][n_kv_head][d]
+// (out [n_head][n_kv]); vec8: d % 8 == 0 and 16-byte aligned kc and q.
+hipError_t launch_kq(const uint16_t *kc, int64_t n_kv, int64_t n_kv_head, int64_t d, const uint16_t *q,
+                     int64_t n_head, bool vec8, float *out, hipStream_t stream);
+
+// acc[b][i] = f16(fma(v[b][i], w[b], acc[b][i])) and acc[b][i] = f16(acc[b][i] * s[b]);
+// vec8: n % 8 == 0 and 16-byte aligned f16 arrays.
+hipError_t launch_mad(uint16_t *acc, const uint16_t *v, const float *w, int64_t nvec, int64_t n, bool vec8,
+                      hipStream_t stream);
+hipError_t launch_scale(uint16_t *acc, const float *s, int64_t nvec, int64_t n, bool vec8, hipStream_t stream);
+
 // fp16 MFMA product of every matrix of g (k % 8 == 0, w and a 16-byte
 // aligned).
 hipError_t launch_mfma(GemmTable g, int64_t k, const uint16_t *a, int64_t n, hipStream_t stream);

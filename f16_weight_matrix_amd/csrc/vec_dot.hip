@@ -29,14 +29,10 @@
 // column (2*k bytes) served from cache.
 #include "f16_round.h"
 #include "kernels.h"
+#include "vec_dot_order.h"
 
 namespace f16wm {
 namespace {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float widen(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
 __device__ __forceinline__ void fma8(float (&acc)[8], u32x4 w, u32x4 a)
 {
@@ -90,58 +86,6 @@ __device__ __forceinline__ float add_tail(float v, const uint16_t *w, const void
         d = d + (double)p;
     }
     return (float)d;
-}
-
-// The 32 chains of one element, spread over LPR lanes (CPL = 32 / LPR chains
-// per lane: global chain c = CPL*j + i for lane j, register i), reduced in the
-// vec_dot tree: c with c^16 and c^8 ((a0+a2)+(a1+a3)), c^4 (low + high half),
-// c^1 then c^2 (the two horizontal adds).  A pairing across lanes is a shuffle
-// by (bit / CPL); a pairing inside a lane adds two registers.  The result is
-// in register 0 of every lane of the row.
-template <int CPL>
-__device__ __forceinline__ float vec_dot_tree(float (&v)[CPL])
-{
-    constexpr int kBits[5] = {16, 8, 4, 1, 2};
-#pragma unroll
-    for (int L = 0; L < 5; L++) {
-        const int b = kBits[L];
-        if (b >= CPL) {
-#pragma unroll
-            for (int i = 0; i < CPL; i++) v[i] = v[i] + __shfl_xor(v[i], b / CPL);
-        } else {
-#pragma unroll
-            for (int i = 0; i < CPL; i++)
-                if ((i & b) == 0) v[i] = v[i] + v[i | b];
-        }
-    }
-    return v[0];
-}
-
-template <int N>
-struct Halves;
-template <>
-struct Halves<8> { typedef u32x4 T; };
-template <>
-struct Halves<4> { typedef uint2 T; };
-template <>
-struct Halves<2> { typedef uint32_t T; };
-template <>
-struct Halves<1> { typedef uint16_t T; };
-
-// acc[i] = fma(w_i, a_i, acc[i]) for the CPL f16 pairs packed in w and a.
-template <int CPL>
-__device__ __forceinline__ void fma_halves(float (&acc)[CPL], typename Halves<CPL>::T w,
-                                           typename Halves<CPL>::T a)
-{
-    typedef _Float16 hv __attribute__((ext_vector_type(CPL == 1 ? 2 : CPL)));
-    if constexpr (CPL == 1) {
-        acc[0] = __builtin_fmaf(widen(w), widen(a), acc[0]);
-    } else {
-        const hv wh = __builtin_bit_cast(hv, w);
-        const hv ah = __builtin_bit_cast(hv, a);
-#pragma unroll
-        for (int i = 0; i < CPL; i++) acc[i] = __builtin_fmaf((float)wh[i], (float)ah[i], acc[i]);
-    }
 }
 
 // LDS-staged GEMV for k % 8 == 0 and 16-byte aligned rows.

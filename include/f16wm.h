@@ -162,6 +162,55 @@ int f16wm_mat_mul_mfma(const uint16_t *w, int64_t rows, int64_t k, const uint16_
 int f16wm_mat_mul_mfma_multi(const f16wm_mat *mats, int32_t count, int64_t k, const uint16_t *a,
                              int64_t n, void *stream);
 
+/* Which columns of a micro-batch leave the last layer (f16wm_mat_mul_out). */
+#define F16WM_OUT_NONE 0
+#define F16WM_OUT_LAST 1
+#define F16WM_OUT_ALL 2
+
+/*
+ * f16wm_mat_mul_out: the last layer's product of a micro-batch of n columns
+ * (a: n x k f16) over only the columns that leave the model.  bankML page
+ * "bankML/forward.rs", section "Why only the output rows leave the last
+ * layer": llama.cpp sends through the last feed-forward block only the rows
+ * it outputs (its inp_out_ids: none, the last, or all), and for F16 weights
+ * that count decides the float order.  mode F16WM_OUT_NONE computes nothing;
+ * F16WM_OUT_LAST computes the last column alone (n >= 1), i.e. vec_dot
+ * (out: rows f32, the bits of f16wm_mat_vec on a + (n-1)*k, which differ
+ * from that column of the full product wherever the full product takes the
+ * tinyBLAS order); F16WM_OUT_ALL is f16wm_mat_mul (out: n x rows f32).
+ * Another mode is F16WM_EINVAL.
+ */
+int f16wm_mat_mul_out(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n, int32_t mode,
+                      float *out, void *stream);
+
+/*
+ * f16wm_kq: attention scores against an f16 K cache in the vec_dot order.
+ * f16 page, Technical usage (vec_dot_u16: vec_dot with the first operand
+ * given as f16 values) and Summary (the attention code uses it for K-cache
+ * rows).  kc: n_kv x n_kv_head x d f16, position-major (one layer's K cache);
+ * q: n_head x d f16 (the rounded queries); out: n_head x n_kv f32 with
+ * out[h * n_kv + p] = vec_dot(kc[p][h / (n_head / n_kv_head)], q[h]).
+ * Requires n_head % n_kv_head == 0 (grouped-query attention) and
+ * n_kv_head <= 65535; d % 8 == 0 with 16-byte aligned kc and q selects the
+ * vectorised kernel, any other d takes the lane-per-chain kernel (same bits).
+ */
+int f16wm_kq(const uint16_t *kc, int64_t n_kv, int64_t n_kv_head, int64_t d, const uint16_t *q, int64_t n_head,
+             float *out, void *stream);
+
+/*
+ * f16wm_mad / f16wm_scale: the f16 V-accumulator updates of the attention
+ * code (f16 page, Technical usage: mad is ggml_vec_mad_f16, scale is
+ * ggml_vec_scale_f16), for nvec vectors of n elements with one f32 weight
+ * (factor) per vector, in place on acc (nvec x n f16, device):
+ *   mad:   acc[b][i] = f16(fma(f32(v[b][i]), w[b], f32(acc[b][i])))
+ *   scale: acc[b][i] = f16(f32(acc[b][i]) * s[b])
+ * each f32 result rounded to f16 as f16wm_to_f16 rounds.  The page names mad
+ * but not its arithmetic: the single fused multiply-add is our reading.
+ * v: nvec x n f16; w, s: nvec f32 in DEVICE memory.  v may not overlap acc.
+ */
+int f16wm_mad(uint16_t *acc, const uint16_t *v, const float *w, int64_t nvec, int64_t n, void *stream);
+int f16wm_scale(uint16_t *acc, const float *s, int64_t nvec, int64_t n, void *stream);
+
 /*
  * f16wm_takes_sgemm: 1 when n >= 2 && rows % 4 == 0 && k % 8 == 0, else 0
  * (f16 page, Technical usage).  Pure host function, no device needed.

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
         "f16wm_to_f16", "f16wm_widen", "f16wm_get_rows", "f16wm_mat_vec", "f16wm_mat_vec_multi",
         "f16wm_mat_vec_f32", "f16wm_mat_vec_multi_f32", "f16wm_mat_mul", "f16wm_mat_mul_mfma",
         "f16wm_mat_mul_multi", "f16wm_mat_mul_mfma_multi", "f16wm_takes_sgemm", "f16wm_last_error",
-        "f16wm_version"])
+        "f16wm_version", "f16wm_mat_mul_out", "f16wm_kq", "f16wm_mad", "f16wm_scale"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -161,6 +161,30 @@ def test_mat_vec_multi_rejects_bad_arguments(L):
     mats[1].out = P + (1 << 20) + 4096
     mats[1].rows = -1
     assert "negative" in _err(L.f16wm_mat_vec_multi(mats, 2, 8, P + (1 << 21), STREAM))
+
+
+def test_next_rows_reject_bad_arguments(L):
+    # the last layer's output columns
+    assert "mode" in _err(L.f16wm_mat_mul_out(P, 4, 8, P + 4096, 3, 7, P + 8192, STREAM))
+    assert "negative" in _err(L.f16wm_mat_mul_out(P, 4, 8, P + 4096, -1, 1, P + 8192, STREAM))
+    assert "empty" in _err(L.f16wm_mat_mul_out(P, 4, 8, P + 4096, 0, 1, P + 8192, STREAM))
+    assert L.f16wm_mat_mul_out(P, 4, 8, P + 4096, 3, 0, None, STREAM) == 0     # none: nothing to do
+    assert "overlap" in _err(L.f16wm_mat_mul_out(P, 4, 8, P + 4096, 3, 1, P + 4, STREAM))
+    # K-cache scores
+    assert "multiple" in _err(L.f16wm_kq(P, 16, 3, 64, P + 65536, 8, P + (1 << 20), STREAM))
+    assert "multiple" in _err(L.f16wm_kq(P, 16, 0, 64, P + 65536, 8, P + (1 << 20), STREAM))
+    assert "negative" in _err(L.f16wm_kq(P, -1, 2, 64, P + 65536, 8, P + (1 << 20), STREAM))
+    assert "null" in _err(L.f16wm_kq(P, 16, 2, 64, None, 8, P + (1 << 20), STREAM))
+    assert "misaligned" in _err(L.f16wm_kq(P + 1, 16, 2, 64, P + 65536, 8, P + (1 << 20), STREAM))
+    assert "overlap" in _err(L.f16wm_kq(P, 16, 2, 64, P + 65536, 8, P + 8, STREAM))
+    assert L.f16wm_kq(P, 0, 2, 64, P + 65536, 8, P + (1 << 20), STREAM) == 0
+    # mad / scale
+    assert "bad size" in _err(L.f16wm_mad(P, P + 4096, P + 8192, -1, 8, STREAM))
+    assert "null" in _err(L.f16wm_mad(P, None, P + 8192, 2, 8, STREAM))
+    assert "overlap" in _err(L.f16wm_mad(P, P + 8, P + 8192, 2, 8, STREAM))
+    assert "misaligned" in _err(L.f16wm_scale(P + 1, P + 8192, 2, 8, STREAM))
+    assert "overlap" in _err(L.f16wm_scale(P, P + 4, 2, 8, STREAM))
+    assert L.f16wm_scale(P, P + 8192, 0, 8, STREAM) == 0
 
 
 def test_empty_products_are_no_ops(L):

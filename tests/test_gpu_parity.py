@@ -566,3 +566,121 @@ def test_llama3_8b_prefill_512(orc):
         say("8B prefill %s: exact ok; mfma err %.3g rel %.3g" % (m, e, rel))
         assert e <= MFMA_TOL
         del wd, ad
+
+
+# ------------------------------------------------------------- next rows
+
+def _with_specials(h: np.ndarray, seed: int) -> np.ndarray:
+    """f16 bit patterns with infinities, a NaN, subnormals, signed zeros and
+    extremes planted at a few seeded positions."""
+    out = h.copy().reshape(-1)
+    sp = np.array([np.inf, -np.inf, np.nan, 6e-8, -6e-8, 0.0, -0.0, 65504.0, -65504.0, 6.1e-5],
+                  dtype=np.float16).view(np.uint16)
+    rng = np.random.default_rng(seed)
+    idx = rng.choice(out.size, size=min(out.size // 16, sp.size), replace=False)
+    out[idx] = sp[:idx.size]
+    return out.reshape(h.shape)
+
+
+@pytest.mark.parametrize("rows,k,n", [(12, 576, 4), (13, 576, 4), (12, 33, 3), (576, 576, 512),
+                                      (4096, 4096, 7), (100, 1000, 1)])
+def test_mat_mul_out_modes(orc, rows, k, n):
+    """The last layer's output columns (forward page, why only the output rows
+    leave the last layer): the last column alone in the vec_dot order, all
+    columns in the shape's order, none computes nothing."""
+    say("mat_mul_out rows=%d k=%d n=%d" % (rows, k, n))
+    w = synth.random_f16(rows * 31 + k, (rows, k), 0.02)
+    a = synth.random_f16(n * 17 + k, (n, k))
+    wd, ad = up16(w), up16(a)
+    assert f16wm.mat_mul_out(wd, ad, f16wm.OUT_NONE) is None
+    last = f16wm.mat_mul_out(wd, ad, f16wm.OUT_LAST).cpu().numpy()
+    assert_bits_equal(last, orc.mat_mul_out(w, a, orc.OUT_LAST), "last column")
+    full = f16wm.mat_mul_out(wd, ad, f16wm.OUT_ALL).cpu().numpy()
+    assert_bits_equal(full, orc.mat_mul_out(w, a, orc.OUT_ALL), "all columns")
+    if orc.takes_sgemm(rows, k, n):
+        # the page's point: the one-row product has different bits
+        assert (last.view(np.uint32) != full[-1].view(np.uint32)).any()
+
+
+@pytest.mark.parametrize("n_kv,n_kv_head,d,n_head,qoff", [
+    (7, 2, 64, 8, 0), (33, 3, 64, 9, 0), (5, 1, 128, 3, 0), (9, 4, 72, 4, 0), (100, 2, 40, 6, 0),
+    (17, 2, 30, 4, 0), (5, 1, 64, 100, 0), (33, 3, 30, 27, 0), (50, 2, 64, 4, 1), (1, 1, 8, 1, 0),
+    (2000, 3, 64, 9, 0), (4096, 8, 128, 32, 0)])
+def test_kq_scores_match_the_oracle(orc, n_kv, n_kv_head, d, n_head, qoff):
+    """vec_dot_u16 over an f16 K cache [n_kv][n_kv_head][d] with grouped-query
+    heads: every score bit for bit; d % 8 != 0 or an unaligned query takes the
+    lane-per-chain kernel, d % 32 != 0 exercises the binary64 tail, more query
+    heads per KV head than a block holds splits them over blocks."""
+    say("kq n_kv=%d n_kv_head=%d d=%d n_head=%d qoff=%d" % (n_kv, n_kv_head, d, n_head, qoff))
+    kc = _with_specials(synth.random_f16(n_kv + d, (n_kv, n_kv_head, d)), 1)
+    q = synth.random_f16(n_head + d, (n_head, d))
+    got = f16wm.kq(up16(kc), up16(q, qoff)).cpu().numpy()
+    assert_bits_equal(got, orc.kq(kc, q), "kq")
+
+
+def test_kq_8b_shaped_long_cache(orc):
+    """An 8B-shaped layer cache at 32768 positions (8 KV heads x 128, 32 query
+    heads): all 1,048,576 scores bit for bit."""
+    n_kv, n_kv_head, d, n_head = 32768, 8, 128, 32
+    kc = synth.random_f16(77, (n_kv, n_kv_head, d))
+    q = synth.random_f16(78, (n_head, d))
+    got = f16wm.kq(up16(kc), up16(q)).cpu().numpy()
+    assert_bits_equal(got, orc.kq(kc, q), "kq 8B 32k")
+
+
+@pytest.mark.parametrize("nvec,n,off", [(6, 67, 0), (32, 128, 0), (32, 128, 1), (1, 8, 0), (1000, 64, 0),
+                                        (3, 5, 0), (4096, 128, 0)])
+def test_mad_and_scale_match_the_oracle(orc, nvec, n, off):
+    """The f16 V-accumulator updates, every element bit for bit (infinities,
+    NaN, subnormals, signed zeros, overflow past 65504 included); n % 8 != 0
+    or an unaligned accumulator takes the one-element kernel."""
+    say("mad/scale nvec=%d n=%d off=%d" % (nvec, n, off))
+    acc = _with_specials(synth.random_f16(nvec + n, (nvec, n), 4.0), 2)
+    v = _with_specials(synth.random_f16(nvec * 3 + n, (nvec, n)), 3)
+    rng = np.random.default_rng(nvec * 7 + n)
+    w = (rng.standard_normal(nvec) * 3).astype(np.float32)
+    s = (rng.standard_normal(nvec) * 2).astype(np.float32)
+    if nvec > 2:
+        w[1], s[1] = 0.0, 1.0
+        w[2], s[2] = 3e4, 1e5          # overflow to infinity in f16
+    ad = up16(acc, off)
+    f16wm.mad(ad, up16(v), up32(w))
+    want = orc.mad(acc, v, w)
+    assert_f16_equal(ad.view(torch.int16).cpu().numpy().view(np.uint16), want, "mad")
+    f16wm.scale(ad, up32(s))
+    want = orc.scale(want, s)
+    assert_f16_equal(ad.view(torch.int16).cpu().numpy().view(np.uint16), want, "scale")
+
+
+def test_mad_and_scale_round_to_f32_before_f16(orc):
+    """Results whose f32 value is an exact f16 tie while the exact value is
+    not: rounding once, straight to f16, gives the other neighbour.  (A
+    compiler fusion of the multiply or FMA with the f16 conversion into one
+    mixed-precision instruction did exactly that.)"""
+    acc = np.array([[0x39b2] * 8], np.uint16)                       # 0.712
+    s = np.array([-0.5759602], np.float32)
+    v = np.array([[0x3c01] * 8], np.uint16)                         # 1 + 2^-10
+    w = np.array([np.float32(1) + np.float32(2.0 ** -23)], np.float32)
+    want_s = orc.scale(acc, s)
+    assert want_s[0, 0] == 0xb690                                   # the tie rounded to even
+    ad = up16(acc)
+    f16wm.scale(ad, up32(s))
+    assert_f16_equal(ad.view(torch.int16).cpu().numpy().view(np.uint16), want_s, "scale tie")
+    for a0 in (0x3c00, 0xbc00, 0x6800, 0x1400):
+        acc2 = np.array([[a0] * 8], np.uint16)
+        ad = up16(acc2)
+        f16wm.mad(ad, up16(v), up32(w))
+        assert_f16_equal(ad.view(torch.int16).cpu().numpy().view(np.uint16), orc.mad(acc2, v, w), "mad")
+
+
+def assert_f16_equal(got: np.ndarray, want: np.ndarray, what: str):
+    """f16 bit patterns equal, NaN compared as "is NaN" (payload propagation
+    through an f32 NaN is the hardware's)."""
+    got, want = np.asarray(got, np.uint16), np.asarray(want, np.uint16)
+    assert got.shape == want.shape, what
+    isnan = lambda b: ((b & 0x7c00) == 0x7c00) & ((b & 0x03ff) != 0)  # noqa: E731
+    same = (got == want) | (isnan(got) & isnan(want))
+    if not same.all():
+        i = tuple(np.argwhere(~same)[0])
+        raise AssertionError("%s: %d of %d differ; first at %s: got 0x%04x want 0x%04x"
+                             % (what, int((~same).sum()), got.size, i, got[i], want[i]))
