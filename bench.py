@@ -269,6 +269,7 @@ def main():
     torch.cuda.synchronize()
     gr_us = ev0.elapsed_time(ev1) * 1e3 / 20
     gr_bytes = N * S["logits"][1] * (2 + 4) + N * 8
+    attn = attention_helpers_leg(f16wm, torch, np, synth, dev, ev)
 
     # the 135M-shaped sequences, as graphs (their own timing; inputs resident)
     small = smollm2_135m_leg(f16wm, torch, np, synth, dev, reps=max(2, args.steps))
@@ -321,8 +322,8 @@ def main():
                      "peak": MFMA_F16_PEAK_TFLOPS, "frac": round(mfma_tflops / MFMA_F16_PEAK_TFLOPS, 4)},
         },
         "smollm2_135m": small,
-        "next_rows": {"get_rows_512x4096": {"avg_us": round(gr_us, 2), "bytes": gr_bytes,
-                                            "GB_s": round(gr_bytes / (gr_us * 1e-6) / 1e9, 1)}},
+        "next_rows": dict({"get_rows_512x4096": {"avg_us": round(gr_us, 2), "bytes": gr_bytes,
+                                                 "GB_s": round(gr_bytes / (gr_us * 1e-6) / 1e9, 1)}}, **attn),
         "setup_s": round(setup_s, 1),
     }
 
@@ -452,6 +453,62 @@ def smollm2_135m_leg(f16wm, torch, np, synth, dev, reps):
     res["weight_copies"] = COPIES
     res["weight_bytes_per_copy"] = weight_bytes
     return res
+
+
+def attention_helpers_leg(f16wm, torch, np, synth, dev, ev):
+    """The f16 attention helpers on an 8B-shaped layer (8 KV heads x 128, 32
+    query heads): vec_dot_u16 scores over a 32768-position f16 K cache (64 MB,
+    a quarter of the last-level cache: a fresh cache copy per launch keeps
+    every launch cold), and mad / scale over the f16 V accumulators of 32768
+    query rows (32 heads x 1024 tokens) of 128 elements."""
+    n_kv, n_kv_head, d, n_head = 32768, 8, 128, 32
+    copies = 6
+    kcs = [torch.from_numpy(synth.random_f16(90 + c, (n_kv, n_kv_head, d)).view(np.int16)).to(dev)
+           .view(torch.float16) for c in range(copies)]
+    q = torch.from_numpy(synth.random_f16(99, (n_head, d)).view(np.int16)).to(dev).view(torch.float16)
+    out = torch.empty((n_head, n_kv), dtype=torch.float32, device=dev)
+    for kc in kcs:
+        f16wm.kq(kc, q, out)
+    reps = 4
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(reps):
+        for kc in kcs:
+            f16wm.kq(kc, q, out)
+    e1.record()
+    torch.cuda.synchronize()
+    kq_us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+    kq_bytes = 2 * n_kv * n_kv_head * d + 2 * n_head * d + 4 * n_head * n_kv
+    del kcs
+    nvec, n = 32768, 128
+    acc = torch.from_numpy(synth.random_f16(100, (nvec, n)).view(np.int16)).to(dev).view(torch.float16)
+    v = torch.from_numpy(synth.random_f16(101, (nvec, n)).view(np.int16)).to(dev).view(torch.float16)
+    w = torch.rand(nvec, device=dev) * 0.01
+    sc = torch.ones(nvec, device=dev)
+    f16wm.mad(acc, v, w)
+    f16wm.scale(acc, sc)
+    reps = 20
+    e0, e1, e2 = ev(), ev(), ev()
+    e0.record()
+    for _ in range(reps):
+        f16wm.mad(acc, v, w)
+    e1.record()
+    for _ in range(reps):
+        f16wm.scale(acc, sc)
+    e2.record()
+    torch.cuda.synchronize()
+    mad_us = e0.elapsed_time(e1) * 1e3 / reps
+    scale_us = e1.elapsed_time(e2) * 1e3 / reps
+    mad_bytes = nvec * n * 6 + nvec * 4
+    scale_bytes = nvec * n * 4 + nvec * 4
+    return {
+        "kq_32768x8x128_32heads": {"avg_us": round(kq_us, 2), "bytes": kq_bytes,
+                                   "GB_s": round(kq_bytes / (kq_us * 1e-6) / 1e9, 1)},
+        "mad_32768x128": {"avg_us": round(mad_us, 2), "bytes": mad_bytes,
+                          "GB_s": round(mad_bytes / (mad_us * 1e-6) / 1e9, 1)},
+        "scale_32768x128": {"avg_us": round(scale_us, 2), "bytes": scale_bytes,
+                            "GB_s": round(scale_bytes / (scale_us * 1e-6) / 1e9, 1)},
+    }
 
 
 def cpu_baseline(host_w, dec, dec_k, S, N, sample_div, gpu_value):

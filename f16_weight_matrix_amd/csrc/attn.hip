@@ -8,16 +8,13 @@
 //
 // kq: out[h][p] = vec_dot(K[p][h / G], q[h]) with the cache laid out
 // position-major, K[p][j][0..d), and G = n_head / n_kv_head query heads per
-// KV head.  A block takes one KV head and a run of positions; its 256 threads
-// form pairs (position, query head) of LPR lanes, lane j of a pair owning
-// chains CPL*j .. CPL*j + CPL - 1 (CPL = 32 / LPR) of that element.  With
-// d % 8 == 0 and 16-byte rows (LPR = 4) a lane reads, per 32-element step,
-// the 16 bytes of its chains from the K row and from the query; the G pairs of
-// one position read the same K bytes, which the same or neighbouring wave
-// loads serve from L1.  Pairs are laid out query-major, so each wave's stores
-// are consecutive positions of one score row.  The reduction is the vec_dot
-// tree (vec_dot_order.h); the d % 32 tail is added in binary64 by lane 0.
-// HBM-bound: the cache is read once, 2 * n_kv * n_kv_head * d bytes.
+// KV head.  For d of 64 or 128 with 16-byte aligned arrays (kq_dma) tiles of
+// consecutive positions -- all KV heads, one contiguous stretch of the cache --
+// stream into LDS by direct loads, and one lane per (position, query head)
+// holds all 32 chains with its query in registers; otherwise (kq_generic) 32
+// lanes per pair each own one chain and read global memory.  The reduction is
+// the vec_dot tree (vec_dot_order.h); a d % 32 tail is added in binary64.
+// The cache is read once: 2 * n_kv * n_kv_head * d bytes.
 //
 // mad / scale: element-wise over nvec vectors of n f16 values with one f32
 // weight (factor) per vector: acc = f16(fma(f32(v), w, f32(acc))) and
@@ -25,6 +22,9 @@
 // (f16_round.h) applied to the finished f32 result (rne_f16_of_result keeps
 // the compiler from fusing the two roundings into one mixed-precision
 // instruction).  HBM-bound: 6 (mad) or 4 (scale) bytes per element.
+#include <atomic>
+
+#include "buffer_rsrc.h"
 #include "f16_round.h"
 #include "kernels.h"
 #include "vec_dot_order.h"
@@ -32,44 +32,163 @@
 namespace f16wm {
 namespace {
 
-template <int LPR>
-__global__ __launch_bounds__(256) void kq_kernel(const uint16_t *__restrict__ kc, int64_t n_kv, int64_t n_kv_head,
-                                                 int64_t d, const uint16_t *__restrict__ q, int64_t G, int P,
-                                                 int GB, float *__restrict__ out)
+// Any d, any alignment: 32 lanes per (position, query head) pair, lane c
+// owning chain c; one position per pair.
+__global__ __launch_bounds__(256) void kq_generic(const uint16_t *__restrict__ kc, int64_t n_kv, int64_t n_kv_head,
+                                                  int64_t d, const uint16_t *__restrict__ q, int64_t G, int P, int GB,
+                                                  float *__restrict__ out)
 {
-    constexpr int CPL = 32 / LPR;
-    typedef typename Halves<CPL>::T HT;
     const int tid = threadIdx.x;
-    const int pair = tid / LPR;
-    const int jj = tid % LPR;
-    const int gl = pair / P;                       // query head within this block
-    const int pp = pair % P;                       // position within this block
-    const int64_t j = blockIdx.y;                  // KV head
+    const int pair = tid / 32;
+    const int c = tid % 32;
+    const int gl = pair / P;
+    const int pp = pair % P;
+    const int64_t j = blockIdx.y;
     const int64_t g = (int64_t)blockIdx.z * GB + gl;
     const int64_t p = (int64_t)blockIdx.x * P + pp;
     const bool valid = gl < GB && g < G && p < n_kv;
     const int64_t h = j * G + (valid ? g : 0);
     const uint16_t *krow = kc + ((valid ? p : 0) * n_kv_head + j) * d;
     const uint16_t *qrow = q + h * d;
-
     const int64_t nsteps = d >> 5;
-    float acc[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; i++) acc[i] = 0.f;
-    if (valid) {
-        for (int64_t t = 0; t < nsteps; t++) {
-            const int64_t e = 32 * t + CPL * jj;
-            fma_halves<CPL>(acc, *reinterpret_cast<const HT *>(krow + e), *reinterpret_cast<const HT *>(qrow + e));
-        }
-    }
-    float v = vec_dot_tree<CPL>(acc);              // every lane of the pair takes part
-    if (valid && jj == 0) {
+    float acc[1] = {0.f};
+    if (valid)
+        for (int64_t t = 0; t < nsteps; t++) acc[0] = __builtin_fmaf(widen(krow[32 * t + c]), widen(qrow[32 * t + c]), acc[0]);
+    float v = vec_dot_tree<1>(acc);
+    if (valid && c == 0) {
         if (d & 31) {
             double s = (double)v;
             for (int64_t i = nsteps * 32; i < d; i++) s = s + (double)(widen(krow[i]) * widen(qrow[i]));
             v = (float)s;
         }
         out[h * n_kv + p] = v;
+    }
+}
+
+// d in {64, 128}, 16-byte aligned cache and queries, n_head <= kKqLanes:
+// one lane per (position, query head) holds all 32 chains of that score, so
+// the whole vec_dot tree is in-lane adds, and keeps its query in registers
+// (a lane's query head never changes).  Blocks are persistent: block b takes
+// tiles b, b + grid, ...; a tile is PB consecutive positions with all their
+// KV heads (one contiguous stretch of the cache; the 32 KB loaded per tile
+// may run into the next tile's first row, which goes unused).
+// One producer wave moves the tiles global -> LDS with buffer_load_dwordx4
+// ... lds (no registers, no ds_write; lane l of a load lands at M0 + 16 l),
+// kKqBuf - 1 tiles ahead, and waits for them; the compute waves meet it at one
+// barrier per tile and never wait on memory counters.  A wave's loads and
+// stores retire in order, so score stores queued behind a tile's loads would
+// lengthen every wait for a tile: the loads get a wave of their own.
+// Rows (one position, one KV head: CH = d / 8 chunks of 16 bytes) are stored
+// with chunk m in slot m ^ (row % CH), so the up-to-16 rows one wave reads at
+// once fall in different banks; lanes of one KV head read the same bytes
+// (broadcast).  Rows past the cache read zero (buffer range check).
+constexpr int kKqLanes = 512;                 // compute lanes per kq_dma block
+constexpr int kKqThreads = kKqLanes + 64;     // and the producer wave
+constexpr int kKqBuf = 3;                     // LDS tile buffers
+constexpr int kKqTile = 32768;                // bytes per tile
+constexpr int kKqLoads = kKqTile / 1024;      // producer loads per tile
+constexpr int kKqPastEnd = 0x7fff0000;        // a tile offset past every cache kq_dma takes
+static_assert((kKqBuf - 2) * kKqLoads <= 63, "the tile wait fits vmcnt");
+
+template <int D>
+__global__ __launch_bounds__(kKqThreads) void kq_dma(const uint16_t *__restrict__ kc, int64_t n_kv, int64_t n_kv_head,
+                                                     const uint16_t *__restrict__ q, int64_t n_head,
+                                                     float *__restrict__ out)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    constexpr int dd = D;
+    const int rowbytes = (int)n_kv_head * dd * 2;  // one position, all KV heads
+    const int PB = kKqTile / rowbytes;             // positions per tile
+    const int64_t ntiles = (n_kv + PB - 1) / PB;
+    // Block b's k-th tile is b + k * grid, held in buffer k % kKqBuf.
+    const int64_t G0 = blockIdx.x, GS = gridDim.x;
+    const int64_t mine = G0 < ntiles ? (ntiles - 1 - G0) / GS + 1 : 0;
+
+    if (wave == kKqLanes / 64) {
+        // The producer.  Load i of a tile fills LDS chunks 64 i + lane: row
+        // (64 i + lane) / CH, slot lane % CH, which holds the row's chunk
+        // slot ^ (row % CH).  Past the block's last tile the same loads read
+        // zero (offset past the cache), so every tile is kKqLoads loads and
+        // the wait counts them.
+        const int lane = tid & 63;
+        constexpr int cs = D == 128 ? 4 : 3;      // log2(CH)
+        constexpr int cm = (1 << cs) - 1;
+        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kc, n_kv * rowbytes);
+        auto issue = [&](int64_t k) {
+            unsigned char *buf = lds + (int)(k % kKqBuf) * kKqTile;
+            const int base = k < mine ? (int)((G0 + k * GS) * PB * rowbytes) : kKqPastEnd;
+#pragma unroll
+            for (int i = 0; i < kKqLoads; i++) {
+                const int row = (64 * i + lane) >> cs;
+                const int goff = ((row << cs) + ((lane & cm) ^ (row & cm))) << 4;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    kr, (__attribute__((address_space(3))) void *)(buf + i * 1024), 16, base + goff, 0, 0, 0);
+            }
+        };
+#pragma unroll
+        for (int k = 0; k < kKqBuf - 1; k++) issue(k);
+        for (int64_t k = 0; k < mine; k++) {
+            // tile k is in LDS (the kKqBuf - 2 younger tiles may still be in
+            // flight); after the barrier the compute waves read it, and they
+            // are done with buffer (k - 1) % kKqBuf, which the next loads fill
+            constexpr int YOUNG = (kKqBuf - 2) * kKqLoads;
+            __builtin_amdgcn_s_waitcnt((YOUNG & 15) | 0x0F70 | ((YOUNG >> 4) << 14));
+            asm volatile("s_barrier" ::: "memory");
+            issue(k + kKqBuf - 1);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);        // the zero loads past the end have landed
+        return;
+    }
+
+    // The compute waves: lane (h, slot) takes query head h of positions
+    // slot, slot + slots, ... of every tile.
+    const int nh = (int)n_head;
+    const int G = (int)(n_head / n_kv_head);
+    constexpr int CH = D / 8;                      // 16-byte chunks per row (8 or 16)
+    constexpr int NS = D / 32;                     // vec_dot steps (2 or 4)
+    const int slots = kKqLanes / nh;               // positions per pass
+    const int h = tid % nh, slot = tid / nh;
+    const bool active = slot < slots;
+    const int j = h / G;                           // this lane's KV head
+
+    // this lane's query, in registers: step t, quarter i = halves 32t + 8i ..
+    u32x4 qv[NS][4];
+#pragma unroll
+    for (int t = 0; t < NS; t++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) qv[t][i] = *reinterpret_cast<const u32x4 *>(q + (int64_t)h * D + 32 * t + 8 * i);
+
+    for (int64_t k = 0; k < mine; k++) {
+        // the LDS reads of tile k - 1 have all returned: each fed the score
+        // stored before this point
+        asm volatile("s_barrier" ::: "memory");
+        const unsigned char *tl = lds + (int)(k % kKqBuf) * kKqTile;
+        const int64_t p0 = (G0 + k * GS) * PB;
+        for (int pp = slot; pp < PB; pp += slots) {
+            const int64_t p = p0 + pp;
+            if (!active || p >= n_kv) continue;
+            const int row = pp * (int)n_kv_head + j;
+            const unsigned char *kl = tl + row * CH * 16;
+            const int sw = row % CH;
+            float acc[32];
+#pragma unroll
+            for (int c = 0; c < 32; c++) acc[c] = 0.f;
+#pragma unroll
+            for (int t = 0; t < NS; t++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    // the query stays packed f16 (the FMAs widen it): a
+                    // widened copy hoisted out of the loop would need
+                    // twice the registers
+                    asm("" : "+v"(qv[t][i]));
+                    const u32x4 kv = *reinterpret_cast<const u32x4 *>(kl + 16 * ((4 * t + i) ^ sw));
+                    float (&a8)[8] = *reinterpret_cast<float (*)[8]>(&acc[8 * i]);
+                    fma_halves<8>(a8, kv, qv[t][i]);
+                }
+            out[(int64_t)h * n_kv + p] = vec_dot_tree<32>(acc);   // all in-lane
+        }
     }
 }
 
@@ -127,6 +246,20 @@ __global__ __launch_bounds__(256) void scale_kernel(uint16_t *__restrict__ acc, 
     }
 }
 
+// Compute units of the current device (looked up once per device).
+int64_t device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c <= 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+        cache[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
 // Enough blocks to fill the GPU several times over; the kernels stride.
 uint32_t elementwise_grid(int64_t items)
 {
@@ -139,18 +272,41 @@ uint32_t elementwise_grid(int64_t items)
 hipError_t launch_kq(const uint16_t *kc, int64_t n_kv, int64_t n_kv_head, int64_t d, const uint16_t *q,
                      int64_t n_head, bool vec8, float *out, hipStream_t stream)
 {
-    const int lpr = vec8 ? 4 : 32;
-    const int pairs = 256 / lpr;                   // pairs per block
+    // LDS kernel: d of 64 or 128, a position row of at most one 32 KB tile,
+    // a cache of at most kKqPastEnd bytes, at most 512 query heads.
+    const int64_t rowbytes = n_kv_head * d * 2;
+    if (vec8 && (d == 64 || d == 128) && n_head <= kKqLanes && rowbytes <= kKqTile &&
+        n_kv * rowbytes <= kKqPastEnd) {
+        static bool once = [] {
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kq_dma<64>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, kKqBuf * kKqTile);
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kq_dma<128>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, kKqBuf * kKqTile);
+            return true;
+        }();
+        (void)once;
+        const int64_t PB = kKqTile / rowbytes;
+        const int64_t ntiles = (n_kv + PB - 1) / PB;
+        // one resident block per CU (the LDS buffers and registers allow one):
+        // every block streams ntiles / CUs tiles through its pipeline
+        const int64_t cus = device_cus();
+        const int64_t gx = ntiles < cus ? ntiles : cus;
+        if (d == 64)
+            kq_dma<64><<<dim3((uint32_t)gx), dim3(kKqThreads), kKqBuf * kKqTile, stream>>>(kc, n_kv, n_kv_head, q,
+                                                                                        n_head, out);
+        else
+            kq_dma<128><<<dim3((uint32_t)gx), dim3(kKqThreads), kKqBuf * kKqTile, stream>>>(kc, n_kv, n_kv_head,
+                                                                                         q, n_head, out);
+        return hipGetLastError();
+    }
+    const int pairs = 8;                           // 32 lanes per pair
     const int64_t G = n_head / n_kv_head;
     const int GB = (int)(G < pairs ? G : pairs);   // query heads per block
     const int P = pairs / GB;                      // positions per block
     const int64_t gx = (n_kv + P - 1) / P, gz = (G + GB - 1) / GB;
     if (gx > 0x7fffffff || n_kv_head > 65535 || gz > 65535) return hipErrorInvalidConfiguration;
     const dim3 grid((uint32_t)gx, (uint32_t)n_kv_head, (uint32_t)gz);
-    if (vec8)
-        kq_kernel<4><<<grid, dim3(256), 0, stream>>>(kc, n_kv, n_kv_head, d, q, G, P, GB, out);
-    else
-        kq_kernel<32><<<grid, dim3(256), 0, stream>>>(kc, n_kv, n_kv_head, d, q, G, P, GB, out);
+    kq_generic<<<grid, dim3(256), 0, stream>>>(kc, n_kv, n_kv_head, d, q, G, P, GB, out);
     return hipGetLastError();
 }
 

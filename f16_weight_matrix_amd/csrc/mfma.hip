@@ -32,6 +32,7 @@
 // the board's power limit); the 8B-shaped n = 512 products reach roughly
 // half of that, limited by keeping the operand stream from L2/HBM ahead of
 // the matrix cores.
+#include "buffer_rsrc.h"
 #include "kernels.h"
 
 namespace f16wm {
@@ -208,18 +209,6 @@ constexpr int kFKS = 64;   // k per stage
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Buffer resource over `bytes` from `base`.  Both are wave-uniform;
-// readfirstlane lets the compiler keep the descriptor in SGPRs.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base, int64_t bytes)
-{
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-    const int nb = __builtin_amdgcn_readfirstlane((int)bytes);
-    // raw buffer: stride 0, num_records = bytes, gfx9 dword3
-    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, nb, 0x00020000);
-}
-
 template <int BM, int BN, int NBUF>
 __global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const uint16_t *__restrict__ a,
                                                  int64_t n, int nct)
@@ -251,8 +240,8 @@ __global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const u
 
     const int64_t arows = n - c0 < BM ? n - c0 : BM;
     const int64_t wrows = rows - r0 < BN ? rows - r0 : BN;
-    const __amdgpu_buffer_rsrc_t ar = tile_rsrc(a + c0 * k, arows * k * 2);
-    const __amdgpu_buffer_rsrc_t wr = tile_rsrc(w + r0 * k, wrows * k * 2);
+    const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(a + c0 * k, arows * k * 2);
+    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(w + r0 * k, wrows * k * 2);
 
     // Load j < LA of this wave fills activation rows (wave * LA + j) * 8 .. +8
     // of a stage, load LA + j weight rows (wave * LW + j) * 8 .. +8.  Byte

@@ -27,6 +27,7 @@
 //
 // HBM-bound: 2*k bytes of weight per row, read once, with the activation
 // column (2*k bytes) served from cache.
+#include "buffer_rsrc.h"
 #include "f16_round.h"
 #include "kernels.h"
 #include "vec_dot_order.h"
@@ -117,19 +118,6 @@ struct LdsCfg {
     static_assert(R * U % 256 == 0, "whole units per thread");
 };
 
-// Buffer resource over `bytes` from `base` (both wave-uniform; readfirstlane
-// lets the compiler keep the descriptor in SGPRs).  An access at or past
-// `bytes` reads zero and touches no memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
-{
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-    const int nb = __builtin_amdgcn_readfirstlane((int)bytes);
-    // raw buffer: stride 0, num_records = bytes, gfx9 dword3
-    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, nb, 0x00020000);
-}
-
 constexpr int kPastEnd = 0x7ffffff0;   // an offset past every resource: reads zero
 
 // Whole activation column in LDS when it is at most 32 KB of f16.
@@ -213,8 +201,8 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const 
     const int64_t rows_m = t.row0[m + 1] - t.row0[m];
     const int64_t r0 = ((int64_t)blockIdx.x - t.tile0[m]) * C::R;
     const int64_t vrows = rows_m - r0 < C::R ? rows_m - r0 : C::R;
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(t.w[m] + r0 * k, vrows * k * 2);
-    const __amdgpu_buffer_rsrc_t ar = make_rsrc(a, k * ESZ);
+    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(t.w[m] + r0 * k, vrows * k * 2);
+    const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(a, k * ESZ);
 
     // Byte offsets of this thread's stage units in stage 0: unit f = row
     // f / U, 16 bytes at element 8 * (f % U); stage s adds 2 * SC * s.

@@ -24,6 +24,20 @@ static __device__ __forceinline__ float widen(uint16_t h) { return (float)__buil
 // c^1 then c^2 (the two horizontal adds).  A pairing across lanes is a shuffle
 // by (bit / CPL); a pairing inside a lane adds two registers.  The result is
 // in register 0 of every lane of the row.
+// x of the lane whose index is this lane's xor M, for M = 1, 2: within a
+// quad, by a DPP quad_perm move (no LDS traffic); other distances use
+// __shfl_xor.
+template <int M>
+__device__ __forceinline__ float lane_xor(float x)
+{
+    if constexpr (M == 1 || M == 2) {
+        constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false));
+    } else {
+        return __shfl_xor(x, M);
+    }
+}
+
 template <int CPL>
 __device__ __forceinline__ float vec_dot_tree(float (&v)[CPL])
 {
@@ -32,8 +46,12 @@ __device__ __forceinline__ float vec_dot_tree(float (&v)[CPL])
     for (int L = 0; L < 5; L++) {
         const int b = kBits[L];
         if (b >= CPL) {
+            const int m = b / CPL;                 // lane distance, constant once unrolled
 #pragma unroll
-            for (int i = 0; i < CPL; i++) v[i] = v[i] + __shfl_xor(v[i], b / CPL);
+            for (int i = 0; i < CPL; i++) {
+                const float o = m == 1 ? lane_xor<1>(v[i]) : m == 2 ? lane_xor<2>(v[i]) : __shfl_xor(v[i], m);
+                v[i] = v[i] + o;
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < CPL; i++)
