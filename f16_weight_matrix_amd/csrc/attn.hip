@@ -65,131 +65,197 @@ __global__ __launch_bounds__(256) void kq_generic(const uint16_t *__restrict__ k
     }
 }
 
-// d in {64, 128}, 16-byte aligned cache and queries, n_head <= kKqLanes:
+// d in {64, 128}, 16-byte aligned cache and queries, n_head <= kKqThreads:
 // one lane per (position, query head) holds all 32 chains of that score, so
-// the whole vec_dot tree is in-lane adds, and keeps its query in registers
+// the whole vec_dot tree is in-lane adds; its query sits in registers as f32
 // (a lane's query head never changes).  Blocks are persistent: block b takes
 // tiles b, b + grid, ...; a tile is PB consecutive positions with all their
 // KV heads (one contiguous stretch of the cache; the 32 KB loaded per tile
-// may run into the next tile's first row, which goes unused).
-// One producer wave moves the tiles global -> LDS with buffer_load_dwordx4
-// ... lds (no registers, no ds_write; lane l of a load lands at M0 + 16 l),
-// kKqBuf - 1 tiles ahead, and waits for them; the compute waves meet it at one
-// barrier per tile and never wait on memory counters.  A wave's loads and
-// stores retire in order, so score stores queued behind a tile's loads would
-// lengthen every wait for a tile: the loads get a wave of their own.
-// Rows (one position, one KV head: CH = d / 8 chunks of 16 bytes) are stored
-// with chunk m in slot m ^ (row % CH), so the up-to-16 rows one wave reads at
-// once fall in different banks; lanes of one KV head read the same bytes
-// (broadcast).  Rows past the cache read zero (buffer range check).
-constexpr int kKqLanes = 512;                 // compute lanes per kq_dma block
-constexpr int kKqThreads = kKqLanes + 64;     // and the producer wave
+// may run into the next tile's first row, which goes unused).  Tiles go
+// global -> LDS with buffer_load_dwordx4 ... lds (no registers, no ds_write;
+// lane l of a load lands at M0 + 16 l), kKqBuf - 1 tiles ahead, marked
+// nontemporal so the streamed cache does not push the partly written score
+// lines out of L2 (their halves merge there before going to HBM).
+// The S lanes of an aligned group (S = 4, 2 or 1, dividing G) hold S query
+// heads of one KV head at one position, so they need the same K row: each
+// reads and widens 1/S of it (chunk 4t + S u + k for lane k of the group),
+// and every FMA takes its K value from the owning lane by a DPP permute
+// inside the quad, folded into v_fmac_f32 (full rate, where the mixed-
+// precision FMA that widens on the fly issues at half rate).
+// Rows (one position, one KV head: CH = d / 8 chunks of 16 bytes) keep chunk
+// m in slot m ^ f(row), f spreading the rows one read instruction touches
+// over the banks.  Rows past the cache read zero (buffer range check).
+constexpr int kKqThreads = 512;               // threads per kq_dma block
 constexpr int kKqBuf = 3;                     // LDS tile buffers
 constexpr int kKqTile = 32768;                // bytes per tile
-constexpr int kKqLoads = kKqTile / 1024;      // producer loads per tile
+constexpr int kKqNW = kKqTile / 1024 / (kKqThreads / 64);   // loads per wave per tile
 constexpr int kKqPastEnd = 0x7fff0000;        // a tile offset past every cache kq_dma takes
-static_assert((kKqBuf - 2) * kKqLoads <= 63, "the tile wait fits vmcnt");
 
+// LDS slot of chunk m of tile row r (an involution in m for each r).
 template <int D>
+__device__ __forceinline__ int kq_slot(int m, int r)
+{
+    if constexpr (D == 128)
+        return m ^ (((r & 3) << 2) | ((r >> 2) & 3));
+    else
+        return m ^ (((r >> 1) & 3) << 1);
+}
+
+// acc = fma(k of lane O of this lane's aligned group of S lanes, q, acc):
+// one v_fmac_f32 whose first operand goes through a DPP quad permute.  The
+// caller keeps the DPP read hazards clear: no VALU write of k in the two
+// instructions before, no VALU write of EXEC in the five before.  Volatile,
+// so these and widen8_ordered keep their program order.
+#define F16WM_FMAC_DPP(PERM)                                                                        \
+    asm volatile("v_fmac_f32_dpp %0, %1, %2 quad_perm:" PERM " row_mask:0xf bank_mask:0xf" : "+v"(acc) \
+                 : "v"(k), "v"(q))
+template <int S, int O>
+__device__ __forceinline__ void fmac_group_lane(float &acc, float k, float q)
+{
+    if constexpr (S == 4) {
+        if constexpr (O == 0) F16WM_FMAC_DPP("[0,0,0,0]");
+        else if constexpr (O == 1) F16WM_FMAC_DPP("[1,1,1,1]");
+        else if constexpr (O == 2) F16WM_FMAC_DPP("[2,2,2,2]");
+        else F16WM_FMAC_DPP("[3,3,3,3]");
+    } else {
+        if constexpr (O == 0) F16WM_FMAC_DPP("[0,0,2,2]");
+        else F16WM_FMAC_DPP("[1,1,3,3]");
+    }
+}
+#undef F16WM_FMAC_DPP
+
+// The eight f16 values of v widened to f32 (exact), element r in f[r], by
+// conversions issued in that order.
+__device__ __forceinline__ void widen8_ordered(float (&f)[8], u32x4 v)
+{
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        asm volatile("v_cvt_f32_f16_e32 %0, %1" : "=v"(f[2 * w]) : "v"(v[w]));
+        asm volatile("v_cvt_f32_f16_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1"
+                     : "=v"(f[2 * w + 1])
+                     : "v"(v[w]));
+    }
+}
+
+template <int D, int S>
 __global__ __launch_bounds__(kKqThreads) void kq_dma(const uint16_t *__restrict__ kc, int64_t n_kv, int64_t n_kv_head,
                                                      const uint16_t *__restrict__ q, int64_t n_head,
                                                      float *__restrict__ out)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    constexpr int CH = D / 8;                      // 16-byte chunks per row
+    constexpr int NS = D / 32;                     // vec_dot steps
+    constexpr int CPS = 4 / S;                     // chunks per step this lane reads
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    constexpr int dd = D;
-    const int rowbytes = (int)n_kv_head * dd * 2;  // one position, all KV heads
+    const int rowbytes = (int)n_kv_head * D * 2;   // one position, all KV heads
     const int PB = kKqTile / rowbytes;             // positions per tile
     const int64_t ntiles = (n_kv + PB - 1) / PB;
-    // Block b's k-th tile is b + k * grid, held in buffer k % kKqBuf.
-    const int64_t G0 = blockIdx.x, GS = gridDim.x;
-    const int64_t mine = G0 < ntiles ? (ntiles - 1 - G0) / GS + 1 : 0;
-
-    if (wave == kKqLanes / 64) {
-        // The producer.  Load i of a tile fills LDS chunks 64 i + lane: row
-        // (64 i + lane) / CH, slot lane % CH, which holds the row's chunk
-        // slot ^ (row % CH).  Past the block's last tile the same loads read
-        // zero (offset past the cache), so every tile is kKqLoads loads and
-        // the wait counts them.
-        const int lane = tid & 63;
-        constexpr int cs = D == 128 ? 4 : 3;      // log2(CH)
-        constexpr int cm = (1 << cs) - 1;
-        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kc, n_kv * rowbytes);
-        auto issue = [&](int64_t k) {
-            unsigned char *buf = lds + (int)(k % kKqBuf) * kKqTile;
-            const int base = k < mine ? (int)((G0 + k * GS) * PB * rowbytes) : kKqPastEnd;
-#pragma unroll
-            for (int i = 0; i < kKqLoads; i++) {
-                const int row = (64 * i + lane) >> cs;
-                const int goff = ((row << cs) + ((lane & cm) ^ (row & cm))) << 4;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    kr, (__attribute__((address_space(3))) void *)(buf + i * 1024), 16, base + goff, 0, 0, 0);
-            }
-        };
-#pragma unroll
-        for (int k = 0; k < kKqBuf - 1; k++) issue(k);
-        for (int64_t k = 0; k < mine; k++) {
-            // tile k is in LDS (the kKqBuf - 2 younger tiles may still be in
-            // flight); after the barrier the compute waves read it, and they
-            // are done with buffer (k - 1) % kKqBuf, which the next loads fill
-            constexpr int YOUNG = (kKqBuf - 2) * kKqLoads;
-            __builtin_amdgcn_s_waitcnt((YOUNG & 15) | 0x0F70 | ((YOUNG >> 4) << 14));
-            asm volatile("s_barrier" ::: "memory");
-            issue(k + kKqBuf - 1);
-        }
-        __builtin_amdgcn_s_waitcnt(0x0F70);        // the zero loads past the end have landed
-        return;
-    }
-
-    // The compute waves: lane (h, slot) takes query head h of positions
-    // slot, slot + slots, ... of every tile.
     const int nh = (int)n_head;
     const int G = (int)(n_head / n_kv_head);
-    constexpr int CH = D / 8;                      // 16-byte chunks per row (8 or 16)
-    constexpr int NS = D / 32;                     // vec_dot steps (2 or 4)
-    const int slots = kKqLanes / nh;               // positions per pass
+    const int slots = kKqThreads / nh;             // positions per pass
     const int h = tid % nh, slot = tid / nh;
     const bool active = slot < slots;
     const int j = h / G;                           // this lane's KV head
+    const int gk = lane & (S - 1);                 // this lane's place in its group
 
-    // this lane's query, in registers: step t, quarter i = halves 32t + 8i ..
-    u32x4 qv[NS][4];
+    // Loads of one tile: load i of wave w fills LDS chunks (w NW + i) 64 + lane.
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kc, n_kv * rowbytes);
+    int goff[kKqNW];
 #pragma unroll
-    for (int t = 0; t < NS; t++)
+    for (int i = 0; i < kKqNW; i++) {
+        const int c = (wave * kKqNW + i) * 64 + lane;
+        const int row = c / CH;
+        goff[i] = (row * CH + kq_slot<D>(c % CH, row)) * 16;
+    }
+    // Block b's k-th tile is b + k * grid, held in buffer k % kKqBuf.  Past
+    // the block's last tile the same loads read zero (offset past the
+    // cache), so every wave issues kKqNW loads per tile and the waits count
+    // them (score stores share the counter: they only lengthen a wait).
+    const int64_t G0 = blockIdx.x, GS = gridDim.x;
+    const int64_t mine = G0 < ntiles ? (ntiles - 1 - G0) / GS + 1 : 0;
+    auto issue = [&](int64_t k) {
+        unsigned char *buf = lds + (int)(k % kKqBuf) * kKqTile;
+        const int base = k < mine ? (int)((G0 + k * GS) * PB * rowbytes) : kKqPastEnd;
 #pragma unroll
-        for (int i = 0; i < 4; i++) qv[t][i] = *reinterpret_cast<const u32x4 *>(q + (int64_t)h * D + 32 * t + 8 * i);
+        for (int i = 0; i < kKqNW; i++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                kr, (__attribute__((address_space(3))) void *)(buf + (wave * kKqNW + i) * 1024), 16,
+                base + goff[i], 0, 0, 2);
+    };
 
+    // this lane's query, widened
+    float qf[D];
+#pragma unroll
+    for (int c = 0; c < CH; c++) {
+        const half8 v = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4 *>(q + (int64_t)h * D + 8 * c));
+#pragma unroll
+        for (int r = 0; r < 8; r++) qf[8 * c + r] = (float)v[r];
+    }
+
+#pragma unroll
+    for (int k = 0; k < kKqBuf - 1; k++) issue(k);
     for (int64_t k = 0; k < mine; k++) {
-        // the LDS reads of tile k - 1 have all returned: each fed the score
-        // stored before this point
+        // this wave's loads of tile k are in LDS, every wave's after the
+        // barrier, and every wave is done with buffer (k - 1) % kKqBuf
+        constexpr int YOUNG = (kKqBuf - 2) * kKqNW;
+        __builtin_amdgcn_s_waitcnt((YOUNG & 15) | 0x0F70 | ((YOUNG >> 4) << 14));
         asm volatile("s_barrier" ::: "memory");
+        issue(k + kKqBuf - 1);
+
         const unsigned char *tl = lds + (int)(k % kKqBuf) * kKqTile;
         const int64_t p0 = (G0 + k * GS) * PB;
         for (int pp = slot; pp < PB; pp += slots) {
             const int64_t p = p0 + pp;
-            if (!active || p >= n_kv) continue;
+            if (!active || p >= n_kv) continue;    // a whole group of S lanes at once
             const int row = pp * (int)n_kv_head + j;
             const unsigned char *kl = tl + row * CH * 16;
-            const int sw = row % CH;
             float acc[32];
 #pragma unroll
             for (int c = 0; c < 32; c++) acc[c] = 0.f;
+            if constexpr (S > 1) asm volatile("s_nop 4");   // an EXEC write before the first DPP read
 #pragma unroll
-            for (int t = 0; t < NS; t++)
+            for (int t = 0; t < NS; t++) {
+                // this lane's chunks of step t, widened: chunk 4t + S u + gk
+                float kf[CPS][8];
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    // the query stays packed f16 (the FMAs widen it): a
-                    // widened copy hoisted out of the loop would need
-                    // twice the registers
-                    asm("" : "+v"(qv[t][i]));
-                    const u32x4 kv = *reinterpret_cast<const u32x4 *>(kl + 16 * ((4 * t + i) ^ sw));
-                    float (&a8)[8] = *reinterpret_cast<float (*)[8]>(&acc[8 * i]);
-                    fma_halves<8>(a8, kv, qv[t][i]);
+                for (int u = 0; u < CPS; u++) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(kl + 16 * kq_slot<D>(4 * t + S * u + gk, row));
+                    if constexpr (S == 1) {
+                        const half8 hv = __builtin_bit_cast(half8, v);
+#pragma unroll
+                        for (int r = 0; r < 8; r++) kf[u][r] = (float)hv[r];
+                    } else {
+                        widen8_ordered(kf[u], v);
+                    }
                 }
+                // quarter i of step t is chunk 4t + i: lane i % S of the
+                // group holds it as its chunk u = i / S; chain 8 i + r.  In
+                // this order FMA number 8 u' + r reads kf[u][r], widened at
+                // least seven instructions earlier.
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int r = 0; r < 8; r++) {
+                        float &a = acc[8 * i + r];
+                        const float kv = kf[i / S][r], qv = qf[32 * t + 8 * i + r];
+                        if constexpr (S == 1)
+                            a = __builtin_fmaf(kv, qv, a);
+                        else if (i % S == 0)
+                            fmac_group_lane<S, 0>(a, kv, qv);
+                        else if (i % S == 1)
+                            fmac_group_lane<S, 1>(a, kv, qv);
+                        else if (i % S == 2)
+                            fmac_group_lane<S, 2>(a, kv, qv);
+                        else
+                            fmac_group_lane<S, 3>(a, kv, qv);
+                    }
+            }
             out[(int64_t)h * n_kv + p] = vec_dot_tree<32>(acc);   // all in-lane
         }
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);            // the zero loads past the end have landed
 }
 
 // Eight elements per thread (n % 8 == 0, 16-byte aligned arrays) or one.
@@ -275,28 +341,29 @@ hipError_t launch_kq(const uint16_t *kc, int64_t n_kv, int64_t n_kv_head, int64_
     // LDS kernel: d of 64 or 128, a position row of at most one 32 KB tile,
     // a cache of at most kKqPastEnd bytes, at most 512 query heads.
     const int64_t rowbytes = n_kv_head * d * 2;
-    if (vec8 && (d == 64 || d == 128) && n_head <= kKqLanes && rowbytes <= kKqTile &&
+    if (vec8 && (d == 64 || d == 128) && n_head <= kKqThreads && rowbytes <= kKqTile &&
         n_kv * rowbytes <= kKqPastEnd) {
+        typedef void (*KqFn)(const uint16_t *, int64_t, int64_t, const uint16_t *, int64_t, float *);
+        static const KqFn fns[2][3] = {{kq_dma<64, 1>, kq_dma<64, 2>, kq_dma<64, 4>},
+                                       {kq_dma<128, 1>, kq_dma<128, 2>, kq_dma<128, 4>}};
         static bool once = [] {
-            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kq_dma<64>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, kKqBuf * kKqTile);
-            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kq_dma<128>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, kKqBuf * kKqTile);
+            for (auto &row : fns)
+                for (KqFn f : row)
+                    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(f),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, kKqBuf * kKqTile);
             return true;
         }();
         (void)once;
+        const int64_t G = n_head / n_kv_head;
+        const int si = G % 4 == 0 ? 2 : G % 2 == 0 ? 1 : 0;   // S = 4, 2, 1 query heads share a K row read
         const int64_t PB = kKqTile / rowbytes;
         const int64_t ntiles = (n_kv + PB - 1) / PB;
         // one resident block per CU (the LDS buffers and registers allow one):
         // every block streams ntiles / CUs tiles through its pipeline
         const int64_t cus = device_cus();
         const int64_t gx = ntiles < cus ? ntiles : cus;
-        if (d == 64)
-            kq_dma<64><<<dim3((uint32_t)gx), dim3(kKqThreads), kKqBuf * kKqTile, stream>>>(kc, n_kv, n_kv_head, q,
-                                                                                        n_head, out);
-        else
-            kq_dma<128><<<dim3((uint32_t)gx), dim3(kKqThreads), kKqBuf * kKqTile, stream>>>(kc, n_kv, n_kv_head,
-                                                                                         q, n_head, out);
+        hipLaunchKernelGGL(fns[d == 128][si], dim3((uint32_t)gx), dim3(kKqThreads), kKqBuf * kKqTile, stream, kc, n_kv,
+                           n_kv_head, q, n_head, out);
         return hipGetLastError();
     }
     const int pairs = 8;                           // 32 lanes per pair

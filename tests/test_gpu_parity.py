@@ -606,7 +606,8 @@ def test_mat_mul_out_modes(orc, rows, k, n):
     (7, 2, 64, 8, 0), (33, 3, 64, 9, 0), (5, 1, 128, 3, 0), (9, 4, 72, 4, 0), (100, 2, 40, 6, 0),
     (17, 2, 30, 4, 0), (5, 1, 64, 100, 0), (33, 3, 30, 27, 0), (50, 2, 64, 4, 1), (1, 1, 8, 1, 0),
     (2000, 3, 64, 9, 0), (4096, 8, 128, 32, 0), (765, 2, 64, 4, 0), (48007, 8, 128, 24, 0),
-    (40, 128, 128, 128, 0), (300, 1, 64, 512, 0), (1000, 3, 128, 12, 0), (3, 1, 128, 513, 0)])
+    (40, 128, 128, 128, 0), (300, 1, 64, 512, 0), (1000, 3, 128, 12, 0), (3, 1, 128, 513, 0),
+    (2500, 4, 128, 8, 0), (3000, 2, 128, 16, 0), (999, 5, 64, 10, 0)])
 def test_kq_scores_match_the_oracle(orc, n_kv, n_kv_head, d, n_head, qoff):
     """vec_dot_u16 over an f16 K cache [n_kv][n_kv_head][d] with grouped-query
     heads: every score bit for bit; d % 8 != 0 or an unaligned query takes the
@@ -614,7 +615,9 @@ def test_kq_scores_match_the_oracle(orc, n_kv, n_kv_head, d, n_head, qoff):
     heads per KV head than a block holds splits them over blocks.  For the
     LDS kernel (d of 64 or 128): a grid of 6 tiles, blocks with 3 tiles
     each, query heads that leave threads idle, one position per 32 KB tile,
-    512 query heads, rows that do not divide the tile; 513 heads fall back."""
+    512 query heads, rows that do not divide the tile; 513 heads fall back.
+    Query heads per KV head divisible by 4, by 2 only, or odd: a K row read
+    shared by a quad of lanes, a pair, or read by each lane."""
     say("kq n_kv=%d n_kv_head=%d d=%d n_head=%d qoff=%d" % (n_kv, n_kv_head, d, n_head, qoff))
     kc = _with_specials(synth.random_f16(n_kv + d, (n_kv, n_kv_head, d)), 1)
     q = synth.random_f16(n_head + d, (n_head, d))
