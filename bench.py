@@ -61,13 +61,25 @@ def cpu_threads() -> int:
 
 
 def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of a kernel source and of the headers beside it that it includes
+    (quoted includes, followed), so a change to any of them shows."""
+    h = hashlib.sha256()
+    seen, todo = set(), [path]
+    while todo:
+        p = todo.pop(0)
+        if p in seen or not os.path.exists(p):
+            continue
+        seen.add(p)
+        text = open(p, "rb").read()
+        h.update(os.path.basename(p).encode() + b"\0" + text)
+        todo += [os.path.join(os.path.dirname(p), inc.decode()) for inc in re.findall(rb'#include "([^"]+)"', text)]
+    return h.hexdigest()[:16]
 
 
 def traffic_record(kernel_src: str):
     """HBM traffic per launch measured with rocprofv3 PMC counters, read from
     profiles/hbm_traffic.md (a fenced json block), valid only for the kernel
-    source it was measured on."""
+    source (and included headers) it was measured on."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
     if not os.path.exists(path):
         return None
