@@ -472,7 +472,9 @@ def attention_helpers_leg(f16wm, torch, np, synth, dev, ev):
     query heads): vec_dot_u16 scores over a 32768-position f16 K cache (64 MB,
     a quarter of the last-level cache: a fresh cache copy per launch keeps
     every launch cold), and mad / scale over the f16 V accumulators of 32768
-    query rows (32 heads x 1024 tokens) of 128 elements."""
+    query rows (32 heads x 1024 tokens) of 128 elements (rotating over copies
+    for the same reason).  Times are per launch of back-to-back launches
+    between two HIP events, launch gaps included."""
     n_kv, n_kv_head, d, n_head = 32768, 8, 128, 32
     copies = 6
     kcs = [torch.from_numpy(synth.random_f16(90 + c, (n_kv, n_kv_head, d)).view(np.int16)).to(dev)
@@ -492,25 +494,34 @@ def attention_helpers_leg(f16wm, torch, np, synth, dev, ev):
     kq_us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
     kq_bytes = 2 * n_kv * n_kv_head * d + 2 * n_head * d + 4 * n_head * n_kv
     del kcs
+    # mad / scale rotate over 48 accumulator (and V) copies, 768 MB in all, so
+    # no launch finds its 8 MB arrays in the last-level cache.
     nvec, n = 32768, 128
-    acc = torch.from_numpy(synth.random_f16(100, (nvec, n)).view(np.int16)).to(dev).view(torch.float16)
-    v = torch.from_numpy(synth.random_f16(101, (nvec, n)).view(np.int16)).to(dev).view(torch.float16)
+    acc0 = torch.from_numpy(synth.random_f16(100, (nvec, n)).view(np.int16)).to(dev).view(torch.float16)
+    v0 = torch.from_numpy(synth.random_f16(101, (nvec, n)).view(np.int16)).to(dev).view(torch.float16)
+    copies = 48
+    accs = [acc0.clone() for _ in range(copies)]
+    vs = [v0.clone() for _ in range(copies)]
     w = torch.rand(nvec, device=dev) * 0.01
     sc = torch.ones(nvec, device=dev)
-    f16wm.mad(acc, v, w)
-    f16wm.scale(acc, sc)
-    reps = 20
+    for acc, v in zip(accs, vs):
+        f16wm.mad(acc, v, w)
+        f16wm.scale(acc, sc)
+    reps = 2
     e0, e1, e2 = ev(), ev(), ev()
     e0.record()
     for _ in range(reps):
-        f16wm.mad(acc, v, w)
+        for acc, v in zip(accs, vs):
+            f16wm.mad(acc, v, w)
     e1.record()
     for _ in range(reps):
-        f16wm.scale(acc, sc)
+        for acc in accs:
+            f16wm.scale(acc, sc)
     e2.record()
     torch.cuda.synchronize()
-    mad_us = e0.elapsed_time(e1) * 1e3 / reps
-    scale_us = e1.elapsed_time(e2) * 1e3 / reps
+    mad_us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+    scale_us = e1.elapsed_time(e2) * 1e3 / (reps * copies)
+    del accs, vs
     mad_bytes = nvec * n * 6 + nvec * 4
     scale_bytes = nvec * n * 4 + nvec * 4
     return {

@@ -312,7 +312,15 @@ __global__ __launch_bounds__(256) void scale_kernel(uint16_t *__restrict__ acc, 
     }
 }
 
-// Compute units of the current device (looked up once per device).
+// Enough blocks to fill the GPU several times over; the kernels stride.
+uint32_t elementwise_grid(int64_t items)
+{
+    const int64_t blocks = (items + 255) / 256;
+    return (uint32_t)(blocks < 8192 ? (blocks > 0 ? blocks : 1) : 8192);
+}
+
+}  // namespace
+
 int64_t device_cus()
 {
     static std::atomic<int> cache[64];
@@ -325,15 +333,6 @@ int64_t device_cus()
     }
     return c;
 }
-
-// Enough blocks to fill the GPU several times over; the kernels stride.
-uint32_t elementwise_grid(int64_t items)
-{
-    const int64_t blocks = (items + 255) / 256;
-    return (uint32_t)(blocks < 8192 ? (blocks > 0 ? blocks : 1) : 8192);
-}
-
-}  // namespace
 
 hipError_t launch_kq(const uint16_t *kc, int64_t n_kv, int64_t n_kv_head, int64_t d, const uint16_t *q,
                      int64_t n_head, bool vec8, float *out, hipStream_t stream)

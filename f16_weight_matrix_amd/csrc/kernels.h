@@ -54,6 +54,9 @@ __device__ __forceinline__ int xcd_tile(int b, int ntiles)
     return xcd * q + (xcd < rem ? xcd : rem) + pos;
 }
 
+// Compute units of the current device (looked up once per device).
+int64_t device_cus();
+
 // Every launcher enqueues on `stream` and returns the hipError_t of the launch.
 hipError_t launch_to_f16(const float *x, uint16_t *y, int64_t count, hipStream_t stream);
 
