@@ -300,11 +300,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 inputs, f32 FMA accumulation (exact ggml orders); fp16 MFMA for the fast path",
+        "dtype": "f32",
         "data": "synthetic: seeded N(0,0.02) f16 weights, N(0,1) f32 activations",
         "config": {
             "workload": "Llama-3-8B-shaped F16 set (q/o 4096x4096, k/v 1024x4096, gate/up 14336x4096, "
                         "down 4096x14336, logits 128256x4096): decode GEMV n=1 + prefill n=512 exact and MFMA",
+            "arithmetic": "f16 weights and rounded f16 activations widened exactly, f32 FMA chains in the exact "
+                          "ggml orders; the MFMA fast path multiplies fp16 into f32",
             "decode_bytes_per_step": decode_bytes,
             "prefill_flops_per_product_set": flops_n512,
             "parallelism": "single GPU",
