@@ -95,8 +95,8 @@ def traffic_record(kernel_src: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (--gpus %d requested); the product shards by "
-              "output rows across GPUs, which is not built here." % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU (--gpus %d requested): the products would shard by output rows "
+              "across GPUs, which is not implemented." % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
