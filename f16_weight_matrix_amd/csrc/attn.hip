@@ -80,8 +80,8 @@ __global__ __launch_bounds__(256) void kq_generic(const uint16_t *__restrict__ k
 // heads of one KV head at one position, so they need the same K row: each
 // reads and widens 1/S of it (chunk 4t + S u + k for lane k of the group),
 // and every FMA takes its K value from the owning lane by a DPP permute
-// inside the quad, folded into v_fmac_f32 (full rate, where the mixed-
-// precision FMA that widens on the fly issues at half rate).
+// inside the quad, folded into v_fmac_f32 (the mixed-precision FMA that
+// widens on the fly issues at about 0.6 of v_fmac_f32's rate here).
 // Rows (one position, one KV head: CH = d / 8 chunks of 16 bytes) keep chunk
 // m in slot m ^ f(row), f spreading the rows one read instruction touches
 // over the banks.  Rows past the cache read zero (buffer range check).
