@@ -330,6 +330,64 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const 
     }
 }
 
+// Short rows (k <= kDirectMaxK, k % 8 == 0, 16-byte aligned): no staging.
+// Four lanes per row, lane j owning chains 8j .. 8j + 7, as in the 64-row
+// LDS blocks; every weight step of the row is loaded straight into registers
+// (16 bytes per lane per step) before the first is used, so the whole row
+// arrives in one memory round trip, while the block rounds the activation
+// column into LDS.  Chains, tree, tail and store as in vec_dot_lds.  For the
+// many small matrices of a small model's decode step, where a launch is a
+// few round trips long.
+constexpr int kDirectMaxK = 640;              // 20 steps of 32
+constexpr int kDirectRows = 16;               // rows per one-wave block
+
+template <bool kF32>
+__global__ __launch_bounds__(64) void vec_dot_direct(RowTable t, int64_t k, const void *__restrict__ a_all)
+{
+    constexpr int MAXS = kDirectMaxK / 32;
+    __shared__ __attribute__((aligned(16))) unsigned char actl[kDirectMaxK * 2];
+    const int tid = threadIdx.x;
+    const int64_t col = blockIdx.y;
+    const void *a = static_cast<const char *>(a_all) + col * k * (kF32 ? 4 : 2);
+    const int j = tid & 3;
+    const int64_t g = (int64_t)blockIdx.x * kDirectRows + (tid >> 2);
+    const bool valid = g < t.row0[t.count];
+    const int m = find_matrix(t, valid ? g : 0);
+    const int64_t r = valid ? g - t.row0[m] : 0;
+    const uint16_t *wrow = t.w[m] + r * k;
+    const int nsteps = (int)(k >> 5);
+
+    u32x4 wv[MAXS];
+#pragma unroll
+    for (int s = 0; s < MAXS; s++)
+        if (valid && s < nsteps) wv[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow + 32 * s + 8 * j));
+    // the column, rounded, 8 elements per thread and round (k % 8 == 0)
+#pragma unroll
+    for (int u0 = 0; u0 < kDirectMaxK / 8; u0 += 64) {
+        const int u = u0 + tid;
+        if (8 * u < k) {
+            u32x4 raw[2];
+            raw[0] = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a) + 8 * u * (kF32 ? 4 : 2));
+            if (kF32) raw[1] = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a) + 8 * u * 4 + 16);
+            *reinterpret_cast<u32x4 *>(actl + 16 * u) = round8<kF32>(raw);
+        }
+    }
+    __syncthreads();
+
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < MAXS; s++)
+        if (s < nsteps) fma_halves<8>(acc, wv[s], *reinterpret_cast<const u32x4 *>(actl + 64 * s + 16 * j));
+    float v = vec_dot_tree<8>(acc);
+    if (valid && j == 0) {
+        if (k & 31) v = add_tail<kF32>(v, wrow, a, (int64_t)nsteps * 32, k);
+        const int64_t rows_m = t.row0[m + 1] - t.row0[m];
+        t.out[m][col * rows_m + r] = v;
+    }
+}
+
 constexpr int kV1Rows = 8;    // rows per 256-thread block, 32 lanes per row
 
 template <bool kF32>
@@ -415,6 +473,23 @@ hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32a
     if (vec8) {
         if (total >= 512 * 64) lpr = 4;
         else if (total >= 512 * 16) lpr = 16;
+    }
+    if (vec8 && k <= kDirectMaxK) {
+        const int64_t bx = (total + kDirectRows - 1) / kDirectRows;
+        if (bx > 0x7fffffff) return hipErrorInvalidConfiguration;
+        for (int64_t c0 = 0; c0 < ncols; c0 += 65535) {
+            const int64_t nc = ncols - c0 < 65535 ? ncols - c0 : 65535;
+            RowTable tc = t;
+            for (int i = 0; i < t.count; i++) tc.out[i] = t.out[i] + c0 * (t.row0[i + 1] - t.row0[i]);
+            const void *ac = static_cast<const char *>(a) + c0 * k * (f32act ? 4 : 2);
+            if (f32act)
+                vec_dot_direct<true><<<dim3((uint32_t)bx, (uint32_t)nc), dim3(64), 0, stream>>>(tc, k, ac);
+            else
+                vec_dot_direct<false><<<dim3((uint32_t)bx, (uint32_t)nc), dim3(64), 0, stream>>>(tc, k, ac);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
     }
     // The LDS kernels address one row tile through 32-bit buffer offsets.
     if (vec8 && (256 / 4) * k * 2 + 65536 > 0x7fff0000) vec8 = false;
