@@ -467,12 +467,13 @@ hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32a
 {
     const int64_t total = t.row0[t.count];
     // Lanes per row: 4 (64-row blocks) when that still gives two blocks per
-    // CU, else 16 when that does, else 32 (measured on the 8B shapes; 8
-    // lanes per row was never faster).
+    // CU, else 16 from 4096 rows on, else 32 (measured on the 8B shapes: 16
+    // lanes beat 32 for the 4096- and 6144-row products by 5-15 %, 8 lanes
+    // per row was never faster).
     int lpr = 32;
     if (vec8) {
         if (total >= 512 * 64) lpr = 4;
-        else if (total >= 512 * 16) lpr = 16;
+        else if (total >= 4096) lpr = 16;
     }
     if (vec8 && k <= kDirectMaxK) {
         const int64_t bx = (total + kDirectRows - 1) / kDirectRows;
