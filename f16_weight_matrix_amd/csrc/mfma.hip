@@ -200,8 +200,9 @@ __global__ __launch_bounds__(256) void mfma_generic(GemmTable g, int64_t k, cons
 //    wave's loads visible and frees the buffer the next loads overwrite.
 //    Launches with fewer 128 x 128 tiles than CUs (q/k/v, o, down at
 //    n = 512) are bound by that wait: one memory round trip per stage
-//    unless several stages are in flight, so they use NBUF = 4 (128 KB of
-//    LDS, one block per CU); the others use NBUF = 2.
+//    unless several stages are in flight, so they use NBUF = 4 (one block
+//    per CU), and 128 x 64 tiles when 128 x 128 would fill at most half the
+//    CUs; the others use NBUF = 2.
 // Measured on this GPU against a register-staged version of the same tiling
 // (three stages in flight through VGPRs, ds_write into LDS): 5-15 % faster,
 // 72 instead of 186 VGPRs, no LDS data-FIFO stalls.
@@ -341,14 +342,15 @@ __global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const u
         }
 }
 
-// Tile offsets of every matrix for a B x B tiling; false past grid.x.
-bool fill_tiles(GemmTable &g, int64_t n, int B, int64_t *nct_out)
+// Tile offsets of every matrix for BM activation columns x BN weight rows
+// per tile; false past grid.x.
+bool fill_tiles(GemmTable &g, int64_t n, int BM, int BN, int64_t *nct_out)
 {
-    const int64_t nct = (n + B - 1) / B;
+    const int64_t nct = (n + BM - 1) / BM;
     int64_t tiles = 0;
     for (int i = 0; i < g.count; i++) {
         g.tile0[i] = (int32_t)tiles;
-        tiles += (g.rows[i] + B - 1) / B * nct;
+        tiles += (g.rows[i] + BN - 1) / BN * nct;
         if (tiles > 0x7fffffff) return false;
     }
     g.tile0[g.count] = (int32_t)tiles;
@@ -364,16 +366,25 @@ hipError_t launch_mfma(GemmTable g, int64_t k, const uint16_t *a, int64_t n, hip
     // tiles (one block per CU, four waves) once there are at least 192 of
     // them (the logits and the grouped gate/up product); 128 x 128 tiles (two
     // blocks per CU) below that, where 256-tiles would leave CUs idle, with
-    // four LDS stages when even the 128-tiles are fewer than the CUs (q/k/v,
-    // o, down).  The fast kernel needs
+    // four LDS stages when even the 128-tiles are fewer than the CUs (q/k/v),
+    // and 128 x 64 tiles with four stages when they would fill at most half
+    // of the CUs (o, down).  The fast kernel needs
     // k % 64 == 0 and 32-bit byte offsets inside one 256-row tile.
     int64_t big = 0;
     for (int i = 0; i < g.count; i++) big += ((g.rows[i] + 255) / 256) * ((n + 255) / 256);
     const bool fast = k % kFKS == 0 && k > 0 && 256 * k * 2 < ((int64_t)1 << 31);
     const int B = fast && big >= 192 ? 256 : 128;
     int64_t nct = 0;
-    if (!fill_tiles(g, n, B, &nct)) return hipErrorInvalidConfiguration;
-    const int64_t tiles = g.tile0[g.count];
+    if (!fill_tiles(g, n, B, B, &nct)) return hipErrorInvalidConfiguration;
+    int64_t tiles = g.tile0[g.count];
+    if (fast && B == 128 && tiles <= 128) {
+        // at most half the CUs would get a 128 x 128 tile (o, down at
+        // n = 512): 128 columns x 64 rows per tile doubles the blocks
+        if (!fill_tiles(g, n, 128, 64, &nct)) return hipErrorInvalidConfiguration;
+        tiles = g.tile0[g.count];
+        mfma_fast<128, 64, 4><<<dim3((uint32_t)tiles), dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+        return hipGetLastError();
+    }
     const dim3 grid((uint32_t)tiles);
     if (!fast)
         mfma_generic<128, 128><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
