@@ -244,7 +244,7 @@ def main():
     torch.cuda.synchronize()
     gemv_ms = [[a.elapsed_time(b) for a, b in ge] for ge in gemv_ms]
 
-    # Roofline of the kernel `value` is about: vec_dot_lds<4>, the logits GEMV
+    # Roofline of the kernel `value` is about: vec_dot_lds<16>, the logits GEMV
     # (70 % of the decode bytes); average duration of its launches: K of them
     # back to back between two HIP events on the stream the library launches
     # on (torch's current), so the events' own cost is spread over K launches.
@@ -265,7 +265,7 @@ def main():
     gemv_all_ms = sum(sum(r) for r in gemv_ms) / K
 
     rec = traffic_record(os.path.join(ROOT, "f16_weight_matrix_amd", "csrc", "vec_dot.hip"))
-    traffic = rec.get("bytes_per_launch") if rec and rec.get("kernel") == "vec_dot_lds<4, true, true>" else None
+    traffic = rec.get("bytes_per_launch") if rec and rec.get("kernel") == "vec_dot_lds<16, true, true>" else None
 
     # Next row beside the step: the embedding lookup of a 512-token micro-batch
     # from the tied 128256x4096 table (get_rows), timed on its own.
@@ -315,7 +315,7 @@ def main():
                       "decode_as_graph": round(dec_graph_avg, 4), "decode_graph_bits_equal_eager": graph_same,
                       "prefill_exact": round(exact_avg, 4), "prefill_mfma": round(mfma_avg, 4)},
         "roofline": {
-            "kernel": "vec_dot_lds<4, true, true> (logits GEMV 128256x4096, f32 column rounded in staging, vec_dot order)",
+            "kernel": "vec_dot_lds<16, true, true> (logits GEMV 128256x4096, f32 column rounded in staging, vec_dot order)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

@@ -11,15 +11,18 @@
 //
 // Each of the 32 chains of an element is a sequential FMA chain, so one chain
 // lives in one GPU lane for the whole row; the tree is a fixed sequence of
-// cross-lane adds.  Both layouts below hold the same 32 chains and apply the
-// same adds, so they give the same bits:
-//   vec8: 4 lanes per row, lane q owns chains 8q..8q+7 and loads the 16 bytes
-//         W[r][32t + 8q .. +7] per step (needs k % 8 == 0, 16-byte alignment).
-//         Tree: lane q + lane q^2 is (a0+a2) / (a1+a3); then lane q + lane q^1;
-//         the low/high and horizontal adds run in-lane.
-//   vec1: 32 lanes per row, lane c owns chain c and loads element 32t + c.
-//         Tree: lane offsets 16, 8 ((a0+a2)+(a1+a3)), 4 (low+high), 1, 2
-//         (horizontal adds).
+// adds.  With LPR lanes per row, lane q of the row owns the CPL = 32 / LPR
+// consecutive chains CPL q .. CPL q + CPL - 1; a tree level pairs chains c
+// and c ^ b, across lanes when b >= CPL and inside a lane otherwise
+// (vec_dot_order.h).  Every layout holds the same 32 chains and applies the
+// same adds, so all give the same bits:
+//   vec_dot_direct (k <= 640, k % 8 == 0, 16-byte alignment): 4 lanes per
+//         row, each loading the 16 bytes W[r][32t + 8q .. +7] of its chains
+//         per step straight into registers.
+//   vec_dot_lds (k % 8 == 0, 16-byte alignment): 16 or 32 lanes per row,
+//         reading their chains from row stages copied into LDS.
+//   vec_dot_v1 (any k, any alignment): 32 lanes per row, lane c loads
+//         element 32t + c.
 // The products of two f16 values are exact in f32, so each chain step's FMA
 // equals an exact product added with one rounding; the widening of f16 inputs
 // is exact (v_cvt_f32_f16 / the f16 operands of v_fma_mix_f32, with f16
@@ -105,9 +108,9 @@ template <int LPR>
 struct LdsCfg {
     static constexpr int R = 256 / LPR;        // rows per block
     static constexpr int CPL = 32 / LPR;       // chains per lane
-    // Weight bytes per stage: 32 KB for the 64-row blocks, 16 KB otherwise
-    // (measured best on MI355X for tall matrices and for 4k-14k rows).
-    static constexpr int STAGE = LPR == 4 ? 32768 : 16384;
+    // Weight bytes per stage: 16 KB (measured best on MI355X against 8 and
+    // 32 KB, with 2 to 8 stages in flight).
+    static constexpr int STAGE = 16384;
     static constexpr int SC = STAGE / 2 / R;   // elements per row per stage
     static constexpr int U = SC / 8;           // 16-byte units per row per stage
     static constexpr int UPT = R * U / 256;    // units per thread per stage
@@ -167,15 +170,9 @@ __device__ __forceinline__ u32x4 round8(const u32x4 (&r)[2])
 // multiply never reads: it stops at the last full 32-element step and the
 // k % 32 tail is read from global memory.
 //
-// The 64-row blocks (LPR = 4) serve only tall matrices with many blocks per
-// CU, where one stage in flight is enough; there the weights come through
-// plain non-temporal global loads, which measured 5 % faster than buffer
-// loads for the 128256 x 4096 logits GEMV (D = 1: the compiler waits for the
-// single stage, so the conditional loads cost nothing).
 template <int LPR>
 struct Depth {
-    static constexpr int D = LPR == 4 ? 1 : 4;
-    static constexpr bool kGlobal = LPR == 4;   // weights by global loads
+    static constexpr int D = 4;
 };
 
 template <int LPR, bool kF32, bool kWhole>
@@ -224,16 +221,8 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const 
         const bool live = s < nstages;
         const int so = live ? (int)(s * C::SC * 2) : 0;
 #pragma unroll
-        for (int p = 0; p < C::UPT; p++) {
-            if (Depth<LPR>::kGlobal) {
-                const int f = p * 256 + tid;
-                if (live && f / C::U < vrows && s * C::SC + 8 * (f % C::U) < k)
-                    wreg[set][p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                        t.w[m] + (r0 + f / C::U) * k + s * C::SC + 8 * (f % C::U)));
-            } else {
-                wreg[set][p] = __builtin_amdgcn_raw_buffer_load_b128(wr, live ? woff[p] + so : kPastEnd, 0, 2);
-            }
-        }
+        for (int p = 0; p < C::UPT; p++)
+            wreg[set][p] = __builtin_amdgcn_raw_buffer_load_b128(wr, live ? woff[p] + so : kPastEnd, 0, 2);
         if (!kWhole) {
             const int ao = live && act_loader ? aoff + (int)(s * C::SC * ESZ) : kPastEnd;
             areg[set][0] = __builtin_amdgcn_raw_buffer_load_b128(ar, ao, 0, 0);
@@ -331,11 +320,11 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const 
 }
 
 // Short rows (k <= kDirectMaxK, k % 8 == 0, 16-byte aligned): no staging.
-// Four lanes per row, lane j owning chains 8j .. 8j + 7, as in the 64-row
-// LDS blocks; every weight step of the row is loaded straight into registers
-// (16 bytes per lane per step) before the first is used, so the whole row
-// arrives in one memory round trip, while the block rounds the activation
-// column into LDS.  Chains, tree, tail and store as in vec_dot_lds.  For the
+// Four lanes per row, lane j owning chains 8j .. 8j + 7 (the 8 elements of
+// one 16-byte piece of each step); every weight step of the row is loaded
+// straight into registers before the first is used, so the whole row arrives
+// in one memory round trip, while the block rounds the activation column
+// into LDS.  Chains, tree, tail and store as in vec_dot_lds.  For the
 // many small matrices of a small model's decode step, where a launch is a
 // few round trips long.
 constexpr int kDirectMaxK = 640;              // 20 steps of 32
@@ -466,15 +455,11 @@ hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32a
                           bool vec8, hipStream_t stream)
 {
     const int64_t total = t.row0[t.count];
-    // Lanes per row: 4 (64-row blocks) when that still gives two blocks per
-    // CU, else 16 from 4096 rows on, else 32 (measured on the 8B shapes: 16
-    // lanes beat 32 for the 4096- and 6144-row products by 5-15 %, 8 lanes
+    // Lanes per row: 16 from 4096 rows on, else 32 (measured on the 8B
+    // shapes: 16 lanes beat 32 by 5-15 % on the 4096- and 6144-row products
+    // and 64-row blocks with 4 lanes by 3 % on the 128256-row logits; 8 lanes
     // per row was never faster).
-    int lpr = 32;
-    if (vec8) {
-        if (total >= 512 * 64) lpr = 4;
-        else if (total >= 4096) lpr = 16;
-    }
+    const int lpr = vec8 && total >= 4096 ? 16 : 32;
     if (vec8 && k <= kDirectMaxK) {
         const int64_t bx = (total + kDirectRows - 1) / kDirectRows;
         if (bx > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -493,7 +478,7 @@ hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32a
         return hipSuccess;
     }
     // The LDS kernels address one row tile through 32-bit buffer offsets.
-    if (vec8 && (256 / 4) * k * 2 + 65536 > 0x7fff0000) vec8 = false;
+    if (vec8 && (256 / 16) * k * 2 + 65536 > 0x7fff0000) vec8 = false;
     const int per = vec8 ? 256 / lpr : kV1Rows;
     RowTable tt = t;
     int64_t bx = (total + per - 1) / per;
@@ -519,8 +504,6 @@ hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32a
                 vec_dot_v1<true><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
             else
                 vec_dot_v1<false><<<grid, dim3(256), 0, stream>>>(tc, k, ac);
-        } else if (lpr == 4) {
-            launch_lds<4>(grid, stream, tc, k, ac, f32act);
         } else if (lpr == 16) {
             launch_lds<16>(grid, stream, tc, k, ac, f32act);
         } else {
