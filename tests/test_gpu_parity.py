@@ -263,8 +263,14 @@ def test_shapes_and_alignment(orc, rows, k, n, woff, aoff):
     [(4096, 4096), (1024, 4096), (1024, 4096)],
     [(1, 96), (63, 96), (64, 96), (65, 96), (7, 96), (200, 96), (3, 96), (129, 96)],
     [(5, 33), (7, 33)],
+    [(4097, 1000), (33, 1000), (100, 1000)],
+    [(17, 576), (40, 576), (3, 576)],
+    [(5000, 4104)],
 ])
 def test_mat_vec_multi(orc, shapes):
+    """Grouped GEMVs, including row tiles that straddle two matrices and
+    k % 32 tails for the 16-lane kernel (4096 rows or more), and ragged
+    groups for the short-row kernel (k <= 640)."""
     k = shapes[0][1]
     ws = [synth.random_f16((21, i, r, k), (r, k), 0.02) for i, (r, _) in enumerate(shapes)]
     a = synth.random_f16((22, k), (k,))
@@ -276,7 +282,8 @@ def test_mat_vec_multi(orc, shapes):
 # ------------------------------------------- f32 activations, rounded inside
 
 @pytest.mark.parametrize("rows,k,off", [(576, 576, 0), (13, 1540, 0), (1000, 4104, 0), (100, 96, 1),
-                                        (64, 33, 3), (4096, 14336, 0), (70000, 64, 0), (5, 8, 2)])
+                                        (64, 33, 3), (4096, 14336, 0), (70000, 64, 0), (5, 8, 2),
+                                        (4099, 1000, 0), (6001, 16376, 0)])
 def test_f32_activation_equals_to_f16_then_product(orc, rows, k, off):
     """mat_vec with an f32 column equals to_f16 then mat_vec, bit for bit
     (edge values of the rounding included; aligned and misaligned columns)."""
