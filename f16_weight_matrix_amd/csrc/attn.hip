@@ -23,6 +23,9 @@
 // the compiler from fusing the two roundings into one mixed-precision
 // instruction).  HBM-bound: 6 (mad) or 4 (scale) bytes per element.
 #include <atomic>
+#include <mutex>
+#include <set>
+#include <utility>
 
 #include "buffer_rsrc.h"
 #include "f16_round.h"
@@ -334,6 +337,17 @@ int64_t device_cus()
     return c;
 }
 
+void allow_dynamic_lds(const void *fn, int bytes)
+{
+    static std::mutex mu;
+    static std::set<std::pair<int, const void *>> done;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.insert({dev, fn}).second)
+        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
 hipError_t launch_kq(const uint16_t *kc, int64_t n_kv, int64_t n_kv_head, int64_t d, const uint16_t *q,
                      int64_t n_head, bool vec8, float *out, hipStream_t stream)
 {
@@ -345,16 +359,9 @@ hipError_t launch_kq(const uint16_t *kc, int64_t n_kv, int64_t n_kv_head, int64_
         typedef void (*KqFn)(const uint16_t *, int64_t, int64_t, const uint16_t *, int64_t, float *);
         static const KqFn fns[2][3] = {{kq_dma<64, 1>, kq_dma<64, 2>, kq_dma<64, 4>},
                                        {kq_dma<128, 1>, kq_dma<128, 2>, kq_dma<128, 4>}};
-        static bool once = [] {
-            for (auto &row : fns)
-                for (KqFn f : row)
-                    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(f),
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, kKqBuf * kKqTile);
-            return true;
-        }();
-        (void)once;
         const int64_t G = n_head / n_kv_head;
         const int si = G % 4 == 0 ? 2 : G % 2 == 0 ? 1 : 0;   // S = 4, 2, 1 query heads share a K row read
+        allow_dynamic_lds(reinterpret_cast<const void *>(fns[d == 128][si]), kKqBuf * kKqTile);
         const int64_t PB = kKqTile / rowbytes;
         const int64_t ntiles = (n_kv + PB - 1) / PB;
         // one resident block per CU (the LDS buffers and registers allow one):

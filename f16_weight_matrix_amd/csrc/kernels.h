@@ -57,6 +57,10 @@ __device__ __forceinline__ int xcd_tile(int b, int ntiles)
 // Compute units of the current device (looked up once per device).
 int64_t device_cus();
 
+// Lets kernel `fn` take `bytes` of dynamic LDS on the current device (the
+// attribute is set once per device and kernel; later calls only look it up).
+void allow_dynamic_lds(const void *fn, int bytes);
+
 // Every launcher enqueues on `stream` and returns the hipError_t of the launch.
 hipError_t launch_to_f16(const float *x, uint16_t *y, int64_t count, hipStream_t stream);
 

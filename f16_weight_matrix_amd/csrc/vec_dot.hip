@@ -413,39 +413,32 @@ __global__ __launch_bounds__(256) void vec_dot_v1(RowTable t, int64_t k, const v
 }
 
 
-// Allow a kernel the LDS it asks for beyond the default dynamic limit.
+// Launches one instantiation with its dynamic LDS allowed first.
 template <typename K>
-void allow_lds(K kernel, size_t bytes)
+void launch_with_lds(K kernel, int max_bytes, dim3 grid, size_t shm, hipStream_t stream, const RowTable &t,
+                     int64_t k, const void *a)
 {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    allow_dynamic_lds(reinterpret_cast<const void *>(kernel), max_bytes);
+    kernel<<<grid, dim3(256), shm, stream>>>(t, k, a);
 }
 
 template <int LPR>
 void launch_lds(dim3 grid, hipStream_t stream, const RowTable &t, int64_t k, const void *a, bool f32act)
 {
     typedef LdsCfg<LPR> C;
-    static bool once = [] {
-        const size_t max_shm = 2 * C::WBYTES + (size_t)kWholeMaxK * 2;
-        allow_lds(vec_dot_lds<LPR, true, true>, max_shm);
-        allow_lds(vec_dot_lds<LPR, false, true>, max_shm);
-        allow_lds(vec_dot_lds<LPR, true, false>, 2 * C::BUFB);
-        allow_lds(vec_dot_lds<LPR, false, false>, 2 * C::BUFB);
-        return true;
-    }();
-    (void)once;
     if (k <= kWholeMaxK) {
+        const int max_shm = 2 * C::WBYTES + (int)kWholeMaxK * 2;
         const size_t shm = 2 * C::WBYTES + (size_t)k * 2;
         if (f32act)
-            vec_dot_lds<LPR, true, true><<<grid, dim3(256), shm, stream>>>(t, k, a);
+            launch_with_lds(vec_dot_lds<LPR, true, true>, max_shm, grid, shm, stream, t, k, a);
         else
-            vec_dot_lds<LPR, false, true><<<grid, dim3(256), shm, stream>>>(t, k, a);
+            launch_with_lds(vec_dot_lds<LPR, false, true>, max_shm, grid, shm, stream, t, k, a);
     } else {
-        const size_t shm = 2 * C::BUFB;
+        const int shm = 2 * C::BUFB;
         if (f32act)
-            vec_dot_lds<LPR, true, false><<<grid, dim3(256), shm, stream>>>(t, k, a);
+            launch_with_lds(vec_dot_lds<LPR, true, false>, shm, grid, shm, stream, t, k, a);
         else
-            vec_dot_lds<LPR, false, false><<<grid, dim3(256), shm, stream>>>(t, k, a);
+            launch_with_lds(vec_dot_lds<LPR, false, false>, shm, grid, shm, stream, t, k, a);
     }
 }
 
