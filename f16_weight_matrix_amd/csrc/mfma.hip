@@ -13,9 +13,9 @@
 // 32 lanes holding one output register cover 32 consecutive r: the stores to
 // out[c*rows + r] are coalesced.
 //
-// Tiling: a 256-thread block computes BM columns x BN rows as 2 x 2 waves;
-// each wave owns (BM/2) x (BN/2) = TM x TN MFMA tiles of 32 x 32.  With
-// 128 x 128 per wave (16 tiles, 256 accumulators in AGPRs) every 16-byte LDS
+// Tiling: a block computes BM columns x BN rows as GM x GN waves (2 x 2 by
+// default); each wave owns (BM/GM) x (BN/GN) = TM x TN MFMA tiles of 32 x 32.
+// With 128 x 128 per wave (16 tiles, 256 accumulators) every 16-byte LDS
 // fragment feeds four MFMAs.  Block b runs on XCD b % 8; tiles are handed out
 // so each XCD walks a contiguous range, and consecutive tiles share one
 // weight-row block, so its weights are read from HBM once and re-read from
@@ -205,20 +205,25 @@ __global__ __launch_bounds__(256) void mfma_generic(GemmTable g, int64_t k, cons
 //    CUs; the others use NBUF = 2.
 // Measured on this GPU against a register-staged version of the same tiling
 // (three stages in flight through VGPRs, ds_write into LDS): 5-15 % faster,
-// 72 instead of 186 VGPRs, no LDS data-FIFO stalls.
+// 72 instead of 186 VGPRs, no LDS data-FIFO stalls.  The 256 x 256 tiles run
+// as 4 x 2 waves of 64 x 128 (two waves per SIMD): with one wave per SIMD the
+// LDS round trips of the fragment reads were exposed (one 4-wave block per CU
+// reaches about half the LDS read bandwidth two blocks reach); eight waves
+// read 1.5 times the fragment bytes per MFMA and were 12-15 % faster.
 constexpr int kFKS = 64;   // k per stage
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int BM, int BN, int NBUF>
-__global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const uint16_t *__restrict__ a,
-                                                 int64_t n, int nct)
+template <int BM, int BN, int NBUF, int GM = 2, int GN = 2>
+__global__ __launch_bounds__(64 * GM * GN) void mfma_fast(GemmTable g, int64_t k, const uint16_t *__restrict__ a,
+                                                          int64_t n, int nct)
 {
-    constexpr int WM = BM / 2, WN = BN / 2;       // wave tile
+    constexpr int NW = GM * GN;                   // waves: GM over the columns, GN over the rows
+    constexpr int WM = BM / GM, WN = BN / GN;     // wave tile
     constexpr int TM = WM / 32, TN = WN / 32;     // 32x32 MFMA tiles per wave
     constexpr int ROWB = kFKS * 2;                // bytes per LDS row (8 chunks)
     constexpr int STAGEB = (BM + BN) * ROWB;      // bytes per stage: [A rows | W rows]
-    constexpr int LA = BM / 32, LW = BN / 32;     // 8-row loads per wave per stage
+    constexpr int LA = BM / (8 * NW), LW = BN / (8 * NW);   // 8-row loads per wave per stage
     constexpr int PAST_END = 0x7ffffff0;          // an offset past every tile: reads zero
     __shared__ __attribute__((aligned(16))) unsigned char smem[NBUF * STAGEB];
 
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(256) void mfma_fast(GemmTable g, int64_t k, const u
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / GN, wn = wave % GN;
     const int lr = lane & 31;
     const int hi = lane >> 5;
 
@@ -363,7 +368,7 @@ bool fill_tiles(GemmTable &g, int64_t n, int BM, int BN, int64_t *nct_out)
 hipError_t launch_mfma(GemmTable g, int64_t k, const uint16_t *a, int64_t n, hipStream_t stream)
 {
     // Tile size, measured on the 8B-shaped products at n = 512: 256 x 256
-    // tiles (one block per CU, four waves) once there are at least 192 of
+    // tiles (one block per CU, eight waves) once there are at least 192 of
     // them (the logits and the grouped gate/up product); 128 x 128 tiles (two
     // blocks per CU) below that, where 256-tiles would leave CUs idle, with
     // four LDS stages when even the 128-tiles are fewer than the CUs (q/k/v),
@@ -389,7 +394,7 @@ hipError_t launch_mfma(GemmTable g, int64_t k, const uint16_t *a, int64_t n, hip
     if (!fast)
         mfma_generic<128, 128><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
     else if (B == 256)
-        mfma_fast<256, 256, 2><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+        mfma_fast<256, 256, 2, 4, 2><<<grid, dim3(64 * 4 * 2), 0, stream>>>(g, k, a, n, (int)nct);
     else if (tiles < 256)   // fewer tiles than CUs: more stages in flight per tile
         mfma_fast<128, 128, 4><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
     else
