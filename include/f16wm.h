@@ -190,9 +190,12 @@ int f16wm_mat_mul_out(const uint16_t *w, int64_t rows, int64_t k, const uint16_t
  * rows).  kc: n_kv x n_kv_head x d f16, position-major (one layer's K cache);
  * q: n_head x d f16 (the rounded queries); out: n_head x n_kv f32 with
  * out[h * n_kv + p] = vec_dot(kc[p][h / (n_head / n_kv_head)], q[h]).
- * Requires n_head % n_kv_head == 0 (grouped-query attention) and
- * n_kv_head <= 65535; d % 8 == 0 with 16-byte aligned kc and q selects the
- * vectorised kernel, any other d takes the lane-per-chain kernel (same bits).
+ * Requires n_head % n_kv_head == 0 (grouped-query attention, else
+ * F16WM_EINVAL) and n_kv_head <= 65535 (else F16WM_EUNSUPPORTED); out may
+ * not overlap kc or q.  d of 64 or 128 with 16-byte aligned kc and q, at
+ * most 512 query heads, a position row (n_kv_head * d halves) of at most
+ * 32 KB and a cache below 2 GB takes the LDS-tiled kernel; any other case
+ * the lane-per-chain kernel (same bits).  Empty outputs are a no-op.
  */
 int f16wm_kq(const uint16_t *kc, int64_t n_kv, int64_t n_kv_head, int64_t d, const uint16_t *q, int64_t n_head,
              float *out, void *stream);
