@@ -326,6 +326,8 @@ def main():
             "algorithmic_bytes_per_launch": gemv_b[li],
             "all_gemv_launches_GB_s": round(sum(gemv_b) / (gemv_all_ms * 1e-3) / 1e9, 1),
             "per_launch": per_launch,
+            "per_launch_note": "each launch between its own pair of HIP events: dispatch and event overhead "
+                               "included (kernel durations: rocprofv3 kernel trace)",
         },
         "gemm_n512": {
             "exact": {"kernel": "tinyblas_mfma (tinyBLAS order, one chain step per fp32 MFMA 32x32x1)",
