@@ -198,6 +198,10 @@ __global__ __launch_bounds__(256) void mfma_generic(GemmTable g, int64_t k, cons
 //    multiplied, stages s + 1 .. s + NBUF - 1 are in flight; a wave waits
 //    for its own loads of stage s (vmcnt) and a plain s_barrier makes every
 //    wave's loads visible and frees the buffer the next loads overwrite.
+//    The loads of the stage that refills it are issued a quarter before
+//    each of the four 16-deep k steps, not all at once after the barrier:
+//    a burst of every wave's loads fills the texture-address queue and
+//    stalls the waves' MFMA issue behind it (5-12 % slower per shape).
 //    Launches with fewer 128 x 128 tiles than CUs (q/k/v, o, down at
 //    n = 512) are bound by that wait: one memory round trip per stage
 //    unless several stages are in flight, so they use NBUF = 4 (one block
@@ -269,15 +273,17 @@ __global__ __launch_bounds__(64 * GM * GN) void mfma_fast(GemmTable g, int64_t k
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-    // Stage s goes to LDS buffer s % NBUF.  Every call issues the same loads
-    // (a stage past the last reads zero and moves no data), so the waits
-    // below can count them.
-    auto issue = [&](int64_t s) {
+    // Stage s goes to LDS buffer s % NBUF; this issues loads j0 .. j1 - 1 of
+    // this wave's LA + LW.  Every stage issues the same loads (a stage past
+    // the last reads zero and moves no data), so the waits below can count
+    // them.
+    auto issue = [&](int64_t s, int j0, int j1) {
         unsigned char *buf = smem + (int)(s % NBUF) * STAGEB;
         const bool live = s < nstages;
         const int so = (int)(s * ROWB);
 #pragma unroll
         for (int j = 0; j < LA + LW; j++) {
+            if (j < j0 || j >= j1) continue;
             const int row0 = j < LA ? (wave * LA + j) * 8 : BM + (wave * LW + j - LA) * 8;
             lds_void *dst = (lds_void *)(buf + row0 * ROWB);
             const int off = live ? voff[j] + so : PAST_END;
@@ -290,12 +296,16 @@ __global__ __launch_bounds__(64 * GM * GN) void mfma_fast(GemmTable g, int64_t k
     // Fragment rows of this lane: wm*WM + i*32 + lr (activations) and
     // BM + wn*WN + j*32 + lr (weights); their swizzle is (lr >> 1) & 7.
     const int sw = (lr >> 1) & 7;
+    // Multiplies stage s; the loads of stage s + NBUF - 1 are issued a
+    // quarter at a time, one quarter before each 16-deep k step.
+    constexpr int NL = LA + LW, NKK = kFKS / 16;
     auto compute = [&](int64_t s) {
         const unsigned char *base = smem + (int)(s % NBUF) * STAGEB;
         const unsigned char *abase = base + (wm * WM + lr) * ROWB;
         const unsigned char *wbase = base + (BM + wn * WN + lr) * ROWB;
 #pragma unroll
-        for (int kk = 0; kk < kFKS / 16; kk++) {
+        for (int kk = 0; kk < NKK; kk++) {
+            issue(s + NBUF - 1, kk * NL / NKK, (kk + 1) * NL / NKK);
             const int ch = 16 * ((2 * kk + hi) ^ sw);
             // let the scheduler interleave the next fragment reads with the MFMAs
             __builtin_amdgcn_iglp_opt(0);
@@ -321,15 +331,14 @@ __global__ __launch_bounds__(64 * GM * GN) void mfma_fast(GemmTable g, int64_t k
     static_assert(YOUNG < 64, "vmcnt range");
     constexpr int WAIT = (YOUNG & 15) | 0x0F70 | ((YOUNG >> 4) << 14);
 #pragma unroll
-    for (int s = 0; s < NBUF - 1; s++) issue(s);
+    for (int s = 0; s < NBUF - 1; s++) issue(s, 0, NL);
     for (int64_t s = 0; s < nstages; s++) {
         // This wave's loads of stage s are in LDS; the barrier makes every
         // wave's loads visible and guarantees stage s - 1 (whose buffer the
-        // next loads fill) is done.  A plain s_barrier: a compiler fence
-        // would also wait for the younger stages.
+        // loads issued during compute(s) fill) is done.  A plain s_barrier:
+        // a compiler fence would also wait for the younger stages.
         __builtin_amdgcn_s_waitcnt(WAIT);
         asm volatile("s_barrier" ::: "memory");
-        issue(s + NBUF - 1);
         compute(s);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // the zero loads past the end have landed
