@@ -23,11 +23,16 @@
 //  - The eight lanes of an element end in the same thread (instruction p,
 //    registers v and v + 16), so the hsum is four in-thread adds in the
 //    page's order, no shuffles.
-//  - A 256-thread block computes 64 weight rows x 128 columns; each wave
-//    32 rows x 64 columns = two 32-column tiles x four instructions x 32
-//    accumulators = 256 accumulators (AGPRs), one wave per SIMD.  Per step a
-//    wave issues eight MFMAs from three 16-byte LDS reads, read one step
-//    ahead so their latency hides behind the matrix core.
+//  - A 256-thread block computes 64 weight rows x 64 columns; each wave
+//    one 32 x 32 tile x four instructions x 32 accumulators = 128
+//    accumulators, and two blocks share a CU (two waves per SIMD, at most
+//    256 registers each).  Per step a wave issues four MFMAs from two
+//    16-byte LDS reads, read one step ahead so their latency hides behind
+//    the matrix core.  Measured against 64 x 128 blocks with one wave per
+//    SIMD (32 x 64 per wave, 256 accumulators): 11 % faster on the 8B-shaped
+//    set at n = 512 (126 instead of 113 TFLOP/s on the large products) and
+//    34 % faster on the 135M-shaped set, whose small matrices then give
+//    twice as many waves; the bits are the same.
 //  - k is staged 64 at a time (8 chain steps) through two LDS buffers holding
 //    the operands already widened to f32 (exactly, once per element and
 //    block): widening inside the step loop would put 24 conversions between
@@ -63,7 +68,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBM = 64;                   // weight rows per block
-constexpr int kBN = 128;                  // activation columns per block
+constexpr int kBN = 64;                   // activation columns per block
 constexpr int kKS = 64;                   // k per stage
 constexpr int kSteps = kKS / 8;           // chain steps per stage
 constexpr int kWG = kBM * 16 + 16;        // bytes of one (step, half) group, weights
@@ -223,17 +228,16 @@ struct Slot {
 static_assert(kHalves <= 4 * kSteps, "more stash entries than MFMA slots");
 
 // Step t's operands: lanes 4h .. 4h + 3 of the thread's weight row and of
-// its two activation columns.
+// its activation column.
 __device__ __forceinline__ void read_step(const char *wl, const char *xl, int t, int h, int wrow, int xcol,
-                                          f32x4 &wa, f32x4 &x0, f32x4 &x1)
+                                          f32x4 &wa, f32x4 &x0)
 {
     wa = *reinterpret_cast<const f32x4 *>(wl + (2 * t + h) * kWG + wrow * 16);
     x0 = *reinterpret_cast<const f32x4 *>(xl + (2 * t + h) * kXG + xcol * 16);
-    x1 = *reinterpret_cast<const f32x4 *>(xl + (2 * t + h) * kXG + (xcol + 32) * 16);
 }
 
 template <bool kBuf>
-__global__ __launch_bounds__(256) void tinyblas_mfma(GemmTable g, int64_t k, const uint16_t *__restrict__ a,
+__global__ __launch_bounds__(256, 2) void tinyblas_mfma(GemmTable g, int64_t k, const uint16_t *__restrict__ a,
                                                      int64_t n, int nct)
 {
     __shared__ __attribute__((aligned(16))) char lds[2 * (kWBuf + kXBuf)];
@@ -251,15 +255,13 @@ __global__ __launch_bounds__(256) void tinyblas_mfma(GemmTable g, int64_t k, con
     const int i = lane & 31;          // row (A) / column (B) within the 32 x 32 tile
     const int h = lane >> 5;          // 0: chain lanes 0..3, 1: chain lanes 4..7
     const int wrow = (wave >> 1) * 32 + i;  // the thread's weight row within the block
-    const int xcol = (wave & 1) * 64 + i;   // its first activation column within the block
+    const int xcol = (wave & 1) * 32 + i;   // its activation column within the block
 
-    f32x32 acc[2][4];
+    f32x32 acc[4];
 #pragma unroll
-    for (int s = 0; s < 2; s++)
+    for (int p = 0; p < 4; p++)
 #pragma unroll
-        for (int p = 0; p < 4; p++)
-#pragma unroll
-            for (int v = 0; v < 32; v++) acc[s][p][v] = 0.f;
+        for (int v = 0; v < 32; v++) acc[p][v] = 0.f;
 
     // Pipeline: during stage st the MFMAs read LDS buffer st % 2, the chunks
     // of stage st + 1 (in registers) are stashed into buffer (st + 1) % 2
@@ -279,19 +281,18 @@ __global__ __launch_bounds__(256) void tinyblas_mfma(GemmTable g, int64_t k, con
         char *nxl = nwl + kWBuf;
         const int64_t kfetch = (st + 2) * kKS;
         // operands one step ahead of the MFMAs that use them
-        f32x4 wa, x0, x1;
-        read_step(wl, xl, 0, h, wrow, xcol, wa, x0, x1);
+        f32x4 wa, x0;
+        read_step(wl, xl, 0, h, wrow, xcol, wa, x0);
         static_for<0, kSteps>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
-            f32x4 nwa, nx0, nx1;
-            if constexpr (t + 1 < kSteps) read_step(wl, xl, t + 1, h, wrow, xcol, nwa, nx0, nx1);
+            f32x4 nwa, nx0;
+            if constexpr (t + 1 < kSteps) read_step(wl, xl, t + 1, h, wrow, xcol, nwa, nx0);
             // keep the reads ahead of this step's MFMAs (their latency then
             // hides behind the matrix core instead of stalling it)
             __builtin_amdgcn_sched_barrier(0);
             static_for<0, 4>([&](auto pc) {
                 constexpr int p = decltype(pc)::value;
-                acc[0][p] = __builtin_amdgcn_mfma_f32_32x32x1f32(wa[p], x0[p], acc[0][p], 0, 0, 0);
-                acc[1][p] = __builtin_amdgcn_mfma_f32_32x32x1f32(wa[p], x1[p], acc[1][p], 0, 0, 0);
+                acc[p] = __builtin_amdgcn_mfma_f32_32x32x1f32(wa[p], x0[p], acc[p], 0, 0, 0);
                 if constexpr (Slot<t, p>::kUsed) {
                     constexpr int q = Slot<t, p>::kUsed ? Slot<t, p>::kQ : 0;
                     __builtin_amdgcn_sched_barrier(0);
@@ -303,7 +304,6 @@ __global__ __launch_bounds__(256) void tinyblas_mfma(GemmTable g, int64_t k, con
             if constexpr (t + 1 < kSteps) {
                 wa = nwa;
                 x0 = nx0;
-                x1 = nx1;
             }
         });
         // buffer (st + 1) % 2 is complete, and every wave is done reading
@@ -315,9 +315,8 @@ __global__ __launch_bounds__(256) void tinyblas_mfma(GemmTable g, int64_t k, con
     // Register v (< 16) of instruction p holds chain lane p and v + 16 lane
     // p + 4 of the element at row (v / 4) * 8 + h * 4 + v % 4, column i.
     const bool o16 = ((uintptr_t)out & 15) == 0;
-#pragma unroll
-    for (int s = 0; s < 2; s++) {
-        const int64_t c = col0 + xcol + 32 * s;
+    {
+        const int64_t c = col0 + xcol;
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             const int64_t r = row0 + (wrow - i) + 8 * q + 4 * h;
@@ -325,8 +324,8 @@ __global__ __launch_bounds__(256) void tinyblas_mfma(GemmTable g, int64_t k, con
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int v = 4 * q + e;
-                o[e] = ((acc[s][0][v] + acc[s][0][v + 16]) + (acc[s][2][v] + acc[s][2][v + 16])) +
-                       ((acc[s][1][v] + acc[s][1][v + 16]) + (acc[s][3][v] + acc[s][3][v + 16]));
+                o[e] = ((acc[0][v] + acc[0][v + 16]) + (acc[2][v] + acc[2][v + 16])) +
+                       ((acc[1][v] + acc[1][v + 16]) + (acc[3][v] + acc[3][v + 16]));
             }
             // rows % 4 == 0 and r % 4 == 0: r < rows covers r .. r + 3
             if (r < rows && c < n) {
