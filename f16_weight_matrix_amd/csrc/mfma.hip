@@ -14,12 +14,13 @@
 // out[c*rows + r] are coalesced.
 //
 // Tiling: a block computes BM columns x BN rows as GM x GN waves (2 x 2 by
-// default); each wave owns (BM/GM) x (BN/GN) = TM x TN MFMA tiles of 32 x 32.
-// With 128 x 128 per wave (16 tiles, 256 accumulators) every 16-byte LDS
-// fragment feeds four MFMAs.  Block b runs on XCD b % 8; tiles are handed out
-// so each XCD walks a contiguous range, and consecutive tiles share one
-// weight-row block, so its weights are read from HBM once and re-read from
-// that XCD's L2.
+// default); each wave owns (BM/GM) x (BN/GN) = TM x TN MFMA tiles of 32 x 32,
+// and each 16-byte LDS fragment it reads feeds TN (activation) or TM
+// (weight) MFMAs: 64 x 128 per wave in the 256 x 256 tiles (eight waves, 128
+// accumulators each), 64 x 64 or 64 x 32 in the smaller ones.  Block b runs
+// on XCD b % 8; tiles are handed out so each XCD walks a contiguous range,
+// and consecutive tiles share one weight-row block, so its weights are read
+// from HBM once and re-read from that XCD's L2.
 //
 // Two kernels: mfma_fast (k % 64 == 0) stages k 64 at a time with direct
 // global-to-LDS loads (see there); mfma_generic (any k % 8 == 0) stages k 32
