@@ -439,6 +439,25 @@ def test_repeatable_bits():
     assert np.array_equal(v1, bits(f16wm.mat_vec(w, a[0])))
 
 
+def test_mfma_bits_do_not_depend_on_the_launch():
+    """Every fp16 MFMA kernel adds an element's 16-deep k slices in the same
+    order, so the tile shape a launch picks (256 x 256 for the grouped gate
+    and up, 128 x 128 with two or four LDS buffers, 128 x 64, a ragged last
+    tile) changes no bit, and a repeated launch gives the same bits."""
+    k, n = 512, 512
+    g = up16(synth.random_f16((61, 14336, k), (14336, k), 0.02))
+    u = up16(synth.random_f16((62, 14336, k), (14336, k), 0.02))
+    a = up16(synth.random_f16((63, n, k), (n, k)))
+    grouped = f16wm.mat_mul_mfma_multi([g, u], a)
+    gb = bits(grouped[0])
+    assert np.array_equal(bits(f16wm.mat_mul_mfma_multi([g, u], a)[0]), gb), "repeated grouped launch"
+    assert np.array_equal(bits(f16wm.mat_mul_mfma(g, a)), gb), "gate alone"
+    assert np.array_equal(bits(f16wm.mat_mul_mfma(u, a)), bits(grouped[1])), "up alone"
+    for rows in (6144, 4100, 4096):
+        got = bits(f16wm.mat_mul_mfma(g[:rows].contiguous(), a))
+        assert np.array_equal(got, gb[:, :rows]), "first %d rows alone" % rows
+
+
 def test_binding_reports_library_errors():
     w = torch.zeros((4, 12), dtype=torch.float16, device=DEV)
     a = torch.zeros((3, 12), dtype=torch.float16, device=DEV)
