@@ -53,8 +53,12 @@
 //    of one weight-row block are consecutive), so each weight row block is
 //    read from HBM once and re-read from that XCD's L2.
 //
+// Launches with few 32 x 32 output tiles use tinyblas_lanes instead (below):
+// one tile per block, its four instructions on four waves.
+//
 // Matrix-core bound: rows*n*k chain steps = 2*rows*n*k flops at the fp32
 // MFMA rate.
+#include "buffer_rsrc.h"
 #include "kernels.h"
 
 #include <type_traits>
@@ -343,11 +347,157 @@ __global__ __launch_bounds__(256, 2) void tinyblas_mfma(GemmTable g, int64_t k, 
     }
 }
 
+// Small grids: one 32 x 32 tile per block, its four instructions split over
+// the block's four waves (wave p carries chain lanes p and p + 4 of all
+// 1024 elements, one MFMA per step), so a product with few tiles runs four
+// times as many waves.  Each chain is the same sequence of FMA steps as in
+// tinyblas_mfma; the eight lanes of an element meet in LDS at the end and
+// are added in the page's order.  Operands are widened once into LDS as
+// [step][chain lane][32 rows + 1 pad] f32: a wave reads 32 consecutive
+// words per half, and the padded stride keeps the stash's ds_write_b32
+// (eight rows x eight steps per wave) free of bank conflicts.
+constexpr int kLT = 32;                         // rows = columns per tile
+constexpr int kLG = kLT + 1;                    // floats per (step, lane) group
+constexpr int kLBuf = kSteps * 8 * kLG * 4;     // bytes of one operand buffer
+// Launches of at most this many 32 x 32 tiles take tinyblas_lanes (measured
+// on the 135M-shaped products at n = 512: q/k/v, o and down, 288-480 tiles,
+// 22-29 % faster; gate/up, 1536 tiles, no faster; 2048 tiles 20 % slower).
+constexpr int64_t kLanesMaxTiles = 1024;
+
+__global__ __launch_bounds__(256) void tinyblas_lanes(GemmTable g, int64_t k, const uint16_t *__restrict__ a,
+                                                      int64_t n, int nct)
+{
+    __shared__ __attribute__((aligned(16))) char lds[2 * 2 * kLBuf];
+
+    int mi, rt, ct;
+    gemm_tile(g, xcd_tile(blockIdx.x, g.tile0[g.count]), nct, mi, rt, ct);
+    const int64_t rows = g.rows[mi];
+    float *__restrict__ out = g.out[mi];
+    const int64_t row0 = (int64_t)rt * kLT;
+    const int64_t col0 = (int64_t)ct * kLT;
+    const uint16_t *w = g.w[mi];
+    const int64_t wr = rows - row0 < kLT ? rows - row0 : kLT;
+    const int64_t xr = n - col0 < kLT ? n - col0 : kLT;
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(w + row0 * k, wr * k * 2);
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a + col0 * k, xr * k * 2);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int p = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's instruction
+    const int i = lane & 31, h = lane >> 5;
+    const int q = p + 4 * h;                                  // this lane's chain lane
+    // the thread's chunk of a stage: row (column) lr, step lt
+    const int lr = tid >> 3, lt = tid & 7;
+    const uint32_t coff = (uint32_t)((lr * k + 8 * lt) * 2);
+
+    f32x32 acc;
+#pragma unroll
+    for (int v = 0; v < 32; v++) acc[v] = 0.f;
+
+    // chunk (lr, lt) of the stage at k0; past k: offset past the resource
+    auto fetch = [&](int64_t k0, u32x4 &cw, u32x4 &cx) {
+        const bool in = k0 + 8 * lt < k;
+        const int off = in ? (int)(coff + (uint32_t)(k0 * 2)) : 0x7ffffff0;
+        cw = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
+        cx = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+    };
+    auto stash = [&](char *buf, const u32x4 &cw, const u32x4 &cx) {
+        const half8 hw = __builtin_bit_cast(half8, cw), hx = __builtin_bit_cast(half8, cx);
+        float *fw = reinterpret_cast<float *>(buf), *fx = reinterpret_cast<float *>(buf + kLBuf);
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            fw[(lt * 8 + e) * kLG + lr] = (float)hw[e];
+            fx[(lt * 8 + e) * kLG + lr] = (float)hx[e];
+        }
+    };
+
+    const int64_t nstages = (k + kKS - 1) / kKS;
+    u32x4 cw, cx;
+    fetch(0, cw, cx);
+    stash(lds, cw, cx);
+    fetch(kKS, cw, cx);
+    __syncthreads();
+    for (int64_t st = 0; st < nstages; st++) {
+        const float *fw = reinterpret_cast<const float *>(lds + (st & 1) * 2 * kLBuf);
+        const float *fx = fw + kLBuf / 4;
+        char *nbuf = lds + ((st + 1) & 1) * 2 * kLBuf;
+        float wa = fw[q * kLG + i], xa = fx[q * kLG + i];
+#pragma unroll
+        for (int t = 0; t < kSteps; t++) {
+            float nw = 0.f, nx = 0.f;
+            if (t + 1 < kSteps) {
+                nw = fw[((t + 1) * 8 + q) * kLG + i];
+                nx = fx[((t + 1) * 8 + q) * kLG + i];
+            }
+            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(wa, xa, acc, 0, 0, 0);
+            if (t == 3) {
+                // stage st + 1 into the other buffer, then fetch st + 2
+                stash(nbuf, cw, cx);
+                fetch((st + 2) * kKS, cw, cx);
+            }
+            wa = nw;
+            xa = nx;
+        }
+        __syncthreads();
+    }
+
+    // Gather: wave p's registers v and v + 16 are chain lanes p and p + 4.
+    // Thread (wave p', lane) then sums registers v = 4p' .. 4p' + 3 of its
+    // lane, i.e. rows 8p' + 4h .. + 3 of column i, from all four waves.
+    float *red = reinterpret_cast<float *>(lds);
+#pragma unroll
+    for (int v = 0; v < 32; v++) red[(p * 32 + v) * 64 + lane] = acc[v];
+    __syncthreads();
+    const int64_t c = col0 + i;
+    const int64_t r = row0 + 8 * p + 4 * h;
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const int v = 4 * p + e;
+        float l[8];
+#pragma unroll
+        for (int w4 = 0; w4 < 4; w4++) {
+            l[w4] = red[(w4 * 32 + v) * 64 + lane];
+            l[w4 + 4] = red[(w4 * 32 + v + 16) * 64 + lane];
+        }
+        o[e] = ((l[0] + l[4]) + (l[2] + l[6])) + ((l[1] + l[5]) + (l[3] + l[7]));
+    }
+    // rows % 4 == 0 and r % 4 == 0: r < rows covers r .. r + 3
+    if (r < rows && c < n) {
+        float *dst = out + c * rows + r;
+        if ((((uintptr_t)dst) & 15) == 0) {
+            *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+            dst[0] = o[0];
+            dst[1] = o[1];
+            dst[2] = o[2];
+            dst[3] = o[3];
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_sgemm(GemmTable g, int64_t k, const uint16_t *a, int64_t n, bool aligned16,
                         hipStream_t stream)
 {
+    // few tiles: one block per 32 x 32 tile, its four instructions on four
+    // waves (aligned operands, 32-row tile resources under 2^31 bytes)
+    if (aligned16 && (int64_t)kLT * k * 2 < ((int64_t)1 << 31)) {
+        const int64_t nct32 = (n + kLT - 1) / kLT;
+        int64_t t32 = 0;
+        for (int m = 0; m < g.count; m++) t32 += (g.rows[m] + kLT - 1) / kLT * nct32;
+        if (t32 <= kLanesMaxTiles) {
+            int64_t acc = 0;
+            for (int m = 0; m < g.count; m++) {
+                g.tile0[m] = (int32_t)acc;
+                acc += (g.rows[m] + kLT - 1) / kLT * nct32;
+            }
+            g.tile0[g.count] = (int32_t)acc;
+            tinyblas_lanes<<<dim3((uint32_t)acc), dim3(256), 0, stream>>>(g, k, a, n, (int)nct32);
+            return hipGetLastError();
+        }
+    }
     const int64_t nct = (n + kBN - 1) / kBN;
     int64_t tiles = 0;
     for (int m = 0; m < g.count; m++) {
