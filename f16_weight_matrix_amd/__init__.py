@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.f16wm_mat_mul.argtypes = [P, I64, I64, P, I64, P, P]
         L.f16wm_mat_mul_mfma.argtypes = [P, I64, I64, P, I64, P, P]
         L.f16wm_mat_mul_multi.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, I64, P]
+        L.f16wm_mat_mul_f32.argtypes = [P, I64, I64, P, I64, P, P]
+        L.f16wm_mat_mul_multi_f32.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, I64, P]
         L.f16wm_mat_mul_mfma_multi.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, I64, P]
         L.f16wm_takes_sgemm.argtypes = [I64, I64, I64]
         L.f16wm_mat_mul_out.argtypes = [P, I64, I64, P, I64, I32, P, P]
@@ -70,8 +72,8 @@ def lib() -> ctypes.CDLL:
         L.f16wm_scale.argtypes = [P, P, I64, I64, P]
         for f in ("f16wm_to_f16", "f16wm_widen", "f16wm_get_rows", "f16wm_mat_vec", "f16wm_mat_vec_multi", "f16wm_mat_vec_f32",
                   "f16wm_mat_vec_multi_f32", "f16wm_mat_mul", "f16wm_mat_mul_mfma", "f16wm_mat_mul_multi",
-                  "f16wm_mat_mul_mfma_multi", "f16wm_takes_sgemm", "f16wm_mat_mul_out", "f16wm_kq", "f16wm_mad",
-                  "f16wm_scale"):
+                  "f16wm_mat_mul_mfma_multi", "f16wm_mat_mul_f32", "f16wm_mat_mul_multi_f32", "f16wm_takes_sgemm",
+                  "f16wm_mat_mul_out", "f16wm_kq", "f16wm_mad", "f16wm_scale"):
             getattr(L, f).restype = ctypes.c_int
         L.f16wm_last_error.restype = ctypes.c_char_p
         L.f16wm_last_error.argtypes = []
@@ -245,9 +247,12 @@ def mat_vec_multi(ws, a: torch.Tensor, outs=None) -> list:
     return outs
 
 
-def _mm(fn, w, a, out):
+def _mm(fn, w, a, out, fn32=None):
     rows, k = _wk(w)
-    _f16(a, "a")
+    if fn32 is not None and _act(a, "a"):
+        fn = fn32
+    else:
+        _f16(a, "a")
     if a.dim() == 1:
         a = a.view(1, -1)
     if a.dim() != 2 or a.shape[1] != k:
@@ -264,8 +269,10 @@ def _mm(fn, w, a, out):
 
 
 def mat_mul(w: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Exact product in ggml's order for the shape: W [rows, k] x A [n, k] -> [n, rows] f32."""
-    return _mm(lib().f16wm_mat_mul, w, a, out)
+    """Exact product in ggml's order for the shape: W [rows, k] x A [n, k] -> [n, rows] f32.
+    A float32 `a` is rounded to f16 inside the same launch (equal to
+    to_f16(a) first, bit for bit)."""
+    return _mm(lib().f16wm_mat_mul, w, a, out, lib().f16wm_mat_mul_f32)
 
 
 def mat_mul_mfma(w: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
@@ -273,7 +280,7 @@ def mat_mul_mfma(w: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = No
     return _mm(lib().f16wm_mat_mul_mfma, w, a, out)
 
 
-def _mm_multi(fn, ws, a, outs):
+def _mm_multi(fn, ws, a, outs, fn32=None):
     ws = list(ws)
     if not 1 <= len(ws) <= MAX_MULTI:
         raise ValueError("1..%d matrices" % MAX_MULTI)
@@ -284,7 +291,10 @@ def _mm_multi(fn, ws, a, outs):
             k = kk
         elif kk != k:
             raise ValueError("all matrices must share k")
-    _f16(a, "a")
+    if fn32 is not None and _act(a, "a"):
+        fn = fn32
+    else:
+        _f16(a, "a")
     if a.dim() == 1:
         a = a.view(1, -1)
     if a.dim() != 2 or a.shape[1] != k:
@@ -311,8 +321,9 @@ def _mm_multi(fn, ws, a, outs):
 
 def mat_mul_multi(ws, a: torch.Tensor, outs=None) -> list:
     """Exact products of several matrices (same k) with one activation block
-    [n, k]: one [n, rows_m] output each, each in its shape's order."""
-    return _mm_multi(lib().f16wm_mat_mul_multi, ws, a, outs)
+    [n, k]: one [n, rows_m] output each, each in its shape's order.  A float32
+    block is rounded to f16 inside the launch (equal to to_f16 first)."""
+    return _mm_multi(lib().f16wm_mat_mul_multi, ws, a, outs, lib().f16wm_mat_mul_multi_f32)
 
 
 def mat_mul_mfma_multi(ws, a: torch.Tensor, outs=None) -> list:

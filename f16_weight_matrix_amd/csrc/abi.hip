@@ -207,8 +207,8 @@ int mat_vec_multi_impl(const char *fn, const f16wm_mat *mats, int32_t count, int
 // shape picks (tinyBLAS when takes_sgemm(rows_m, k, n), else vec_dot); one
 // launch when every matrix takes the tinyBLAS order.  mfma: the matrix-core
 // product of every matrix in one launch.
-int mat_mul_impl(const char *fn, const f16wm_mat *mats, int32_t count, int64_t k, const uint16_t *a,
-                 int64_t n, bool mfma, void *stream)
+int mat_mul_impl(const char *fn, const f16wm_mat *mats, int32_t count, int64_t k, const void *a,
+                 bool f32act, int64_t n, bool mfma, void *stream)
 {
     if (count < 1 || count > F16WM_MAX_MULTI)
         return fail(F16WM_EINVAL, "%s: count %d outside 1..%d", fn, (int)count, F16WM_MAX_MULTI);
@@ -221,7 +221,8 @@ int mat_mul_impl(const char *fn, const f16wm_mat *mats, int32_t count, int64_t k
             snprintf(name, sizeof name, "%s", fn);
         else
             snprintf(name, sizeof name, "%s[%d]", fn, m);
-        if (int rc = check_product(name, mats[m].w, mats[m].rows, k, a, 2, n, mats[m].out, &we, &ae, &oe))
+        if (int rc = check_product(name, mats[m].w, mats[m].rows, k, a, f32act ? 4 : 2, n, mats[m].out, &we, &ae,
+                                   &oe))
             return rc;
         for (int j = 0; j < m; j++) {
             const Span sm = span(mats[m].out, mats[m].rows * n * 4);
@@ -251,8 +252,9 @@ int mat_mul_impl(const char *fn, const f16wm_mat *mats, int32_t count, int64_t k
         g.count++;
         all_sgemm = all_sgemm && f16wm_takes_sgemm(mats[m].rows, k, n);
     }
-    if (mfma) return launched(fn, f16wm::launch_mfma(g, k, a, n, (hipStream_t)stream));
-    if (all_sgemm) return launched(fn, f16wm::launch_sgemm(g, k, a, n, al16, (hipStream_t)stream));
+    if (mfma)
+        return launched(fn, f16wm::launch_mfma(g, k, static_cast<const uint16_t *>(a), n, (hipStream_t)stream));
+    if (all_sgemm) return launched(fn, f16wm::launch_sgemm(g, k, a, n, al16, f32act, (hipStream_t)stream));
     // other orders: one launch per matrix, each in its own order
     for (int m = 0; m < g.count; m++) {
         hipError_t e;
@@ -262,7 +264,7 @@ int mat_mul_impl(const char *fn, const f16wm_mat *mats, int32_t count, int64_t k
             one.w[0] = g.w[m];
             one.rows[0] = g.rows[m];
             one.out[0] = g.out[m];
-            e = f16wm::launch_sgemm(one, k, a, n, al16, (hipStream_t)stream);
+            e = f16wm::launch_sgemm(one, k, a, n, al16, f32act, (hipStream_t)stream);
         } else {
             f16wm::RowTable t = {};
             t.count = 1;
@@ -270,7 +272,7 @@ int mat_mul_impl(const char *fn, const f16wm_mat *mats, int32_t count, int64_t k
             t.out[0] = g.out[m];
             t.row0[0] = 0;
             t.row0[1] = g.rows[m];
-            e = f16wm::launch_vec_dot(t, k, a, false, n, k % 8 == 0 && al16, (hipStream_t)stream);
+            e = f16wm::launch_vec_dot(t, k, a, f32act, n, k % 8 == 0 && al16, (hipStream_t)stream);
         }
         if (e != hipSuccess) return launched(fn, e);
     }
@@ -345,26 +347,39 @@ int f16wm_mat_mul(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a,
                   float *out, void *stream)
 {
     const f16wm_mat m = {w, rows, out};
-    return mat_mul_impl("f16wm_mat_mul", &m, 1, k, a, n, false, stream);
+    return mat_mul_impl("f16wm_mat_mul", &m, 1, k, a, false, n, false, stream);
+}
+
+int f16wm_mat_mul_f32(const uint16_t *w, int64_t rows, int64_t k, const float *x, int64_t n, float *out,
+                      void *stream)
+{
+    const f16wm_mat m = {w, rows, out};
+    return mat_mul_impl("f16wm_mat_mul_f32", &m, 1, k, x, true, n, false, stream);
 }
 
 int f16wm_mat_mul_multi(const f16wm_mat *mats, int32_t count, int64_t k, const uint16_t *a, int64_t n,
                         void *stream)
 {
-    return mat_mul_impl("f16wm_mat_mul_multi", mats, count, k, a, n, false, stream);
+    return mat_mul_impl("f16wm_mat_mul_multi", mats, count, k, a, false, n, false, stream);
+}
+
+int f16wm_mat_mul_multi_f32(const f16wm_mat *mats, int32_t count, int64_t k, const float *x, int64_t n,
+                            void *stream)
+{
+    return mat_mul_impl("f16wm_mat_mul_multi_f32", mats, count, k, x, true, n, false, stream);
 }
 
 int f16wm_mat_mul_mfma(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n,
                        float *out, void *stream)
 {
     const f16wm_mat m = {w, rows, out};
-    return mat_mul_impl("f16wm_mat_mul_mfma", &m, 1, k, a, n, true, stream);
+    return mat_mul_impl("f16wm_mat_mul_mfma", &m, 1, k, a, false, n, true, stream);
 }
 
 int f16wm_mat_mul_mfma_multi(const f16wm_mat *mats, int32_t count, int64_t k, const uint16_t *a,
                              int64_t n, void *stream)
 {
-    return mat_mul_impl("f16wm_mat_mul_mfma_multi", mats, count, k, a, n, true, stream);
+    return mat_mul_impl("f16wm_mat_mul_mfma_multi", mats, count, k, a, false, n, true, stream);
 }
 
 int f16wm_mat_mul_out(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a, int64_t n, int32_t mode,
@@ -379,7 +394,7 @@ int f16wm_mat_mul_out(const uint16_t *w, int64_t rows, int64_t k, const uint16_t
     if (mode == F16WM_OUT_NONE) return ok();
     if (mode == F16WM_OUT_ALL) {
         const f16wm_mat m = {w, rows, out};
-        return mat_mul_impl(fn, &m, 1, k, a, n, false, stream);
+        return mat_mul_impl(fn, &m, 1, k, a, false, n, false, stream);
     }
     if (n < 1) return fail(F16WM_EINVAL, "%s: the last column of an empty micro-batch", fn);
     int64_t off;

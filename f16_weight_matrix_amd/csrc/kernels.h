@@ -73,8 +73,10 @@ hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32a
                           bool vec8, hipStream_t stream);
 
 // tinyBLAS order for every matrix of g (rows % 4 == 0, k % 8 == 0, n >= 2
-// checked by the caller).  aligned16: every w and a are 16-byte aligned.
-hipError_t launch_sgemm(GemmTable g, int64_t k, const uint16_t *a, int64_t n, bool aligned16,
+// checked by the caller).  aligned16: every w and a are 16-byte aligned.  The
+// activation block a [n][k] is f16 bit patterns, or f32 values (f32act)
+// rounded in the kernel exactly as launch_to_f16 rounds them.
+hipError_t launch_sgemm(GemmTable g, int64_t k, const void *a, int64_t n, bool aligned16, bool f32act,
                         hipStream_t stream);
 
 // Exact f16 -> f32 of count values, and of rows ids[0..nids) of W (rows x k)

@@ -59,6 +59,7 @@
 // Matrix-core bound: rows*n*k chain steps = 2*rows*n*k flops at the fp32
 // MFMA rate.
 #include "buffer_rsrc.h"
+#include "f16_round.h"
 #include "kernels.h"
 
 #include <type_traits>
@@ -96,64 +97,104 @@ __device__ __forceinline__ u32x4 load8(const uint16_t *p)
 }
 
 // Where a stage's chunks come from.  kBuf: 16-byte aligned operands and
-// kBN * k * 2 < 2^31 bytes, read with raw buffer loads whose resource covers
+// kBN * k * ESZ < 2^31 bytes, read with raw buffer loads whose resource covers
 // just this tile's rows (or columns); an offset at or past the resource's
 // end returns zero, so rows past the matrix, columns past n and chunks past
 // k need no branch.  Otherwise plain loads guarded by the same conditions.
-template <bool kBuf>
+// kF32: the activation block holds f32 values (ESZ = 4 bytes), rounded to f16
+// when a chunk is stashed; a chunk is then 32 bytes, kept raw as two
+// 16-byte halves until the stash.  Otherwise f16 patterns (ESZ = 2), one
+// 16-byte half.
+template <bool kBuf, bool kF32>
 struct Src {
-    const uint16_t *w, *a;
+    static constexpr int ESZ = kF32 ? 4 : 2;
+    const uint16_t *w;
+    const char *a;
     int64_t rows, n, k, row0, col0;
     __amdgpu_buffer_rsrc_t rw, rx;
 
-    __device__ __forceinline__ Src(const uint16_t *w_, int64_t rows_, const uint16_t *a_, int64_t n_, int64_t k_,
+    __device__ __forceinline__ Src(const uint16_t *w_, int64_t rows_, const void *a_, int64_t n_, int64_t k_,
                                    int64_t row0_, int64_t col0_)
-        : w(w_), a(a_), rows(rows_), n(n_), k(k_), row0(row0_), col0(col0_)
+        : w(w_), a(static_cast<const char *>(a_)), rows(rows_), n(n_), k(k_), row0(row0_), col0(col0_)
     {
         if constexpr (kBuf) {
             const int64_t wr = rows - row0 < kBM ? rows - row0 : kBM;
             const int64_t xr = n - col0 < kBN ? n - col0 : kBN;
-            // raw buffer: stride 0, num_records = bytes, gfx9 dword3
-            rw = __builtin_amdgcn_make_buffer_rsrc((void *)(w + row0 * k), (short)0, (int)(wr * k * 2), 0x00020000);
-            rx = __builtin_amdgcn_make_buffer_rsrc((void *)(a + col0 * k), (short)0, (int)(xr * k * 2), 0x00020000);
+            rw = buffer_rsrc(w + row0 * k, wr * k * 2);
+            rx = buffer_rsrc(a + col0 * k * ESZ, xr * k * ESZ);
         }
     }
 
-    // Byte offset of chunk (r, gk) in a tile resource; a chunk past k gets
-    // bit 31 set, which puts it past the resource's end (under 2^31 bytes).
-    __device__ __forceinline__ uint32_t offset(int r, int64_t gk) const
+    // Byte offset of chunk (r, gk) in a tile resource of esz-byte elements; a
+    // chunk past k gets bit 31 set, which puts it past the resource's end
+    // (under 2^31 bytes).
+    __device__ __forceinline__ uint32_t offset(int r, int64_t gk, int esz) const
     {
-        return (uint32_t)((r * k + gk) * 2) | (gk < k ? 0u : 0x80000000u);
+        return (uint32_t)((r * k + gk) * esz) | (gk < k ? 0u : 0x80000000u);
     }
 
-    // chunk (r, elements gk .. gk + 7) of the weight tile / activation tile
+    // chunk (r, elements gk .. gk + 7) of the weight tile
     __device__ __forceinline__ u32x4 wchunk(int r, int64_t gk) const
     {
         if constexpr (kBuf) {
-            return __builtin_amdgcn_raw_buffer_load_b128(rw, (int)offset(r, gk), 0, 0);
+            return __builtin_amdgcn_raw_buffer_load_b128(rw, (int)offset(r, gk, 2), 0, 0);
         } else {
             u32x4 v = {0u, 0u, 0u, 0u};
             if (row0 + r < rows && gk < k) v = load8<false>(w + (row0 + r) * k + gk);
             return v;
         }
     }
-    __device__ __forceinline__ u32x4 xchunk(int r, int64_t gk) const
+    // chunk (r, elements gk .. gk + 7) of the activation tile, raw
+    __device__ __forceinline__ void xchunk(int r, int64_t gk, u32x4 (&x)[2]) const
     {
         if constexpr (kBuf) {
-            return __builtin_amdgcn_raw_buffer_load_b128(rx, (int)offset(r, gk), 0, 0);
+            const uint32_t off = offset(r, gk, ESZ);
+            x[0] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+            if constexpr (kF32) x[1] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(off + 16), 0, 0);
         } else {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (col0 + r < n && gk < k) v = load8<false>(a + (col0 + r) * k + gk);
-            return v;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            x[0] = z;
+            if constexpr (kF32) x[1] = z;
+            if (col0 + r < n && gk < k) {
+                if constexpr (kF32) {
+                    const uint32_t *f = reinterpret_cast<const uint32_t *>(a) + (col0 + r) * k + gk;
+                    x[0] = u32x4{f[0], f[1], f[2], f[3]};
+                    x[1] = u32x4{f[4], f[5], f[6], f[7]};
+                } else {
+                    x[0] = load8<false>(reinterpret_cast<const uint16_t *>(a) + (col0 + r) * k + gk);
+                }
+            }
         }
     }
 };
 
+// Four activation values of a stashed chunk (elements 4 hf .. 4 hf + 3),
+// widened to f32: the f16 patterns as they are, or f32 values rounded to f16
+// first by the rounding every kernel shares (so the result equals
+// f16wm_to_f16 followed by the f16 product).  Elements are copied out of the
+// vectors before use: this clang miscompiles __builtin_bit_cast applied to a
+// vector element in place.
+__device__ __forceinline__ float widen_h(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+template <bool kF32>
+__device__ __forceinline__ f32x4 act4(const u32x4 (&x)[2], int hf)
+{
+    if constexpr (kF32) {
+        const u32x4 p = hf ? x[1] : x[0];
+        const uint32_t e0 = p[0], e1 = p[1], e2 = p[2], e3 = p[3];
+        return f32x4{widen_h(rne_f16(__uint_as_float(e0))), widen_h(rne_f16(__uint_as_float(e1))),
+                     widen_h(rne_f16(__uint_as_float(e2))), widen_h(rne_f16(__uint_as_float(e3)))};
+    } else {
+        const half8 h = __builtin_bit_cast(half8, x[0]);
+        return f32x4{(float)h[4 * hf], (float)h[4 * hf + 1], (float)h[4 * hf + 2], (float)h[4 * hf + 3]};
+    }
+}
+
 // Global -> registers for the stage at k0.  Chunk c of a tile is row (or
 // column) c / kSteps, elements 8 (c % kSteps) .. + 7 of the stage; zero past
 // rows, n or k (k % 8 == 0: a chunk is all inside k or all outside).
-template <bool kBuf>
-__device__ __forceinline__ void fetch_stage(u32x4 (&wr)[kWPT], u32x4 (&xr)[kXPT], const Src<kBuf> &src,
+template <bool kBuf, bool kF32>
+__device__ __forceinline__ void fetch_stage(u32x4 (&wr)[kWPT], u32x4 (&xr)[kXPT][2], const Src<kBuf, kF32> &src,
                                             int64_t k0, int tid)
 {
 #pragma unroll
@@ -164,21 +205,21 @@ __device__ __forceinline__ void fetch_stage(u32x4 (&wr)[kWPT], u32x4 (&xr)[kXPT]
 #pragma unroll
     for (int p = 0; p < kXPT; p++) {
         const int c = p * 256 + tid;
-        xr[p] = src.xchunk(c / kSteps, k0 + 8 * (c % kSteps));
+        src.xchunk(c / kSteps, k0 + 8 * (c % kSteps), xr[p]);
     }
 }
 
 // Chunk j (weights first) of the stage at k0 into its register.
-template <bool kBuf, int j>
-__device__ __forceinline__ void fetch_chunk(u32x4 (&wr)[kWPT], u32x4 (&xr)[kXPT], const Src<kBuf> &src, int64_t k0,
-                                            int tid)
+template <bool kBuf, bool kF32, int j>
+__device__ __forceinline__ void fetch_chunk(u32x4 (&wr)[kWPT], u32x4 (&xr)[kXPT][2], const Src<kBuf, kF32> &src,
+                                            int64_t k0, int tid)
 {
     constexpr bool isw = j < kWPT;
     const int c = (isw ? j : j - kWPT) * 256 + tid;
     if constexpr (isw)
         wr[isw ? j : 0] = src.wchunk(c / kSteps, k0 + 8 * (c % kSteps));
     else
-        xr[isw ? 0 : j - kWPT] = src.xchunk(c / kSteps, k0 + 8 * (c % kSteps));
+        src.xchunk(c / kSteps, k0 + 8 * (c % kSteps), xr[isw ? 0 : j - kWPT]);
 }
 
 // Registers -> LDS, widened exactly to f32 once here.  Entry (t, h, row) is
@@ -190,19 +231,24 @@ __device__ __forceinline__ void fetch_chunk(u32x4 (&wr)[kWPT], u32x4 (&xr)[kXPT]
 // (weights first), elements 4 (q % 2) .. + 3.
 constexpr int kHalves = 2 * (kWPT + kXPT);
 
-template <int q>
-__device__ __forceinline__ void stash_half(char *wl, char *xl, const u32x4 (&wr)[kWPT], const u32x4 (&xr)[kXPT],
-                                           int tid)
+template <bool kF32, int q>
+__device__ __forceinline__ void stash_half(char *wl, char *xl, const u32x4 (&wr)[kWPT],
+                                           const u32x4 (&xr)[kXPT][2], int tid)
 {
     constexpr int cq = q / 2, hf = q % 2;
     constexpr bool isw = cq < kWPT;
     const int c = (isw ? cq : cq - kWPT) * 256 + tid;
     const int r = c / kSteps, t = c % kSteps;
-    const half8 x = __builtin_bit_cast(half8, isw ? wr[isw ? cq : 0] : xr[isw ? 0 : cq - kWPT]);
+    f32x4 v;
+    if constexpr (isw) {
+        const half8 x = __builtin_bit_cast(half8, wr[isw ? cq : 0]);
+        v = f32x4{(float)x[4 * hf], (float)x[4 * hf + 1], (float)x[4 * hf + 2], (float)x[4 * hf + 3]};
+    } else {
+        v = act4<kF32>(xr[isw ? 0 : cq - kWPT], hf);
+    }
     char *grp = isw ? wl : xl;
     const int gsize = isw ? kWG : kXG;
-    *reinterpret_cast<f32x4 *>(grp + (2 * t + hf) * gsize + r * 16) =
-        f32x4{(float)x[4 * hf], (float)x[4 * hf + 1], (float)x[4 * hf + 2], (float)x[4 * hf + 3]};
+    *reinterpret_cast<f32x4 *>(grp + (2 * t + hf) * gsize + r * 16) = v;
 }
 
 // Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
@@ -215,10 +261,11 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
+template <bool kF32>
 __device__ __forceinline__ void stash_stage(char *wl, char *xl, const u32x4 (&wr)[kWPT],
-                                            const u32x4 (&xr)[kXPT], int tid)
+                                            const u32x4 (&xr)[kXPT][2], int tid)
 {
-    static_for<0, kHalves>([&](auto qc) { stash_half<decltype(qc)::value>(wl, xl, wr, xr, tid); });
+    static_for<0, kHalves>([&](auto qc) { stash_half<kF32, decltype(qc)::value>(wl, xl, wr, xr, tid); });
 }
 
 // The stage's 4 * kSteps MFMA slots (step t, instruction p) share out the
@@ -240,9 +287,9 @@ __device__ __forceinline__ void read_step(const char *wl, const char *xl, int t,
     x0 = *reinterpret_cast<const f32x4 *>(xl + (2 * t + h) * kXG + xcol * 16);
 }
 
-template <bool kBuf>
-__global__ __launch_bounds__(256, 2) void tinyblas_mfma(GemmTable g, int64_t k, const uint16_t *__restrict__ a,
-                                                     int64_t n, int nct)
+template <bool kBuf, bool kF32>
+__global__ __launch_bounds__(256, 2) void tinyblas_mfma(GemmTable g, int64_t k, const void *__restrict__ a,
+                                                        int64_t n, int nct)
 {
     __shared__ __attribute__((aligned(16))) char lds[2 * (kWBuf + kXBuf)];
 
@@ -252,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void tinyblas_mfma(GemmTable g, int64_t k, 
     float *__restrict__ out = g.out[mi];
     const int64_t row0 = (int64_t)rt * kBM;
     const int64_t col0 = (int64_t)ct * kBN;
-    const Src<kBuf> src(g.w[mi], rows, a, n, k, row0, col0);
+    const Src<kBuf, kF32> src(g.w[mi], rows, a, n, k, row0, col0);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -273,10 +320,10 @@ __global__ __launch_bounds__(256, 2) void tinyblas_mfma(GemmTable g, int64_t k, 
     // chunk of stage st + 2, which so has a whole stage to arrive.  Chunks
     // past k are zero, so the last stages need no special case.
     const int64_t nstages = (k + kKS - 1) / kKS;
-    u32x4 wreg[kWPT], xreg[kXPT];
-    fetch_stage<kBuf>(wreg, xreg, src, 0, tid);
-    stash_stage(lds, lds + kWBuf, wreg, xreg, tid);
-    fetch_stage<kBuf>(wreg, xreg, src, kKS, tid);
+    u32x4 wreg[kWPT], xreg[kXPT][2];
+    fetch_stage<kBuf, kF32>(wreg, xreg, src, 0, tid);
+    stash_stage<kF32>(lds, lds + kWBuf, wreg, xreg, tid);
+    fetch_stage<kBuf, kF32>(wreg, xreg, src, kKS, tid);
     __syncthreads();
     for (int64_t st = 0; st < nstages; st++) {
         const char *wl = lds + (st & 1) * (kWBuf + kXBuf);
@@ -300,8 +347,8 @@ __global__ __launch_bounds__(256, 2) void tinyblas_mfma(GemmTable g, int64_t k, 
                 if constexpr (Slot<t, p>::kUsed) {
                     constexpr int q = Slot<t, p>::kUsed ? Slot<t, p>::kQ : 0;
                     __builtin_amdgcn_sched_barrier(0);
-                    stash_half<q>(nwl, nxl, wreg, xreg, tid);
-                    if constexpr (q % 2 == 1) fetch_chunk<kBuf, q / 2>(wreg, xreg, src, kfetch, tid);
+                    stash_half<kF32, q>(nwl, nxl, wreg, xreg, tid);
+                    if constexpr (q % 2 == 1) fetch_chunk<kBuf, kF32, q / 2>(wreg, xreg, src, kfetch, tid);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             });
@@ -364,7 +411,8 @@ constexpr int kLBuf = kSteps * 8 * kLG * 4;     // bytes of one operand buffer
 // 22-29 % faster; gate/up, 1536 tiles, no faster; 2048 tiles 20 % slower).
 constexpr int64_t kLanesMaxTiles = 1024;
 
-__global__ __launch_bounds__(256) void tinyblas_lanes(GemmTable g, int64_t k, const uint16_t *__restrict__ a,
+template <bool kF32>
+__global__ __launch_bounds__(256) void tinyblas_lanes(GemmTable g, int64_t k, const void *__restrict__ a,
                                                       int64_t n, int nct)
 {
     __shared__ __attribute__((aligned(16))) char lds[2 * 2 * kLBuf];
@@ -379,7 +427,8 @@ __global__ __launch_bounds__(256) void tinyblas_lanes(GemmTable g, int64_t k, co
     const int64_t wr = rows - row0 < kLT ? rows - row0 : kLT;
     const int64_t xr = n - col0 < kLT ? n - col0 : kLT;
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(w + row0 * k, wr * k * 2);
-    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a + col0 * k, xr * k * 2);
+    constexpr int ESZ = kF32 ? 4 : 2;             // activation element bytes
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(static_cast<const char *>(a) + col0 * k * ESZ, xr * k * ESZ);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -388,31 +437,36 @@ __global__ __launch_bounds__(256) void tinyblas_lanes(GemmTable g, int64_t k, co
     const int q = p + 4 * h;                                  // this lane's chain lane
     // the thread's chunk of a stage: row (column) lr, step lt
     const int lr = tid >> 3, lt = tid & 7;
-    const uint32_t coff = (uint32_t)((lr * k + 8 * lt) * 2);
+    const uint32_t coff = (uint32_t)((lr * k + 8 * lt) * 2);       // weights
+    const uint32_t cxoff = (uint32_t)((lr * k + 8 * lt) * ESZ);    // activations
 
     f32x32 acc;
 #pragma unroll
     for (int v = 0; v < 32; v++) acc[v] = 0.f;
 
-    // chunk (lr, lt) of the stage at k0; past k: offset past the resource
-    auto fetch = [&](int64_t k0, u32x4 &cw, u32x4 &cx) {
+    // chunk (lr, lt) of the stage at k0 (activations raw: one or two 16-byte
+    // halves); past k: offset past the resource
+    auto fetch = [&](int64_t k0, u32x4 &cw, u32x4 (&cx)[2]) {
         const bool in = k0 + 8 * lt < k;
         const int off = in ? (int)(coff + (uint32_t)(k0 * 2)) : 0x7ffffff0;
+        const int xoff = in ? (int)(cxoff + (uint32_t)(k0 * ESZ)) : 0x7ffffff0;
         cw = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
-        cx = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+        cx[0] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, 0, 0);
+        if constexpr (kF32) cx[1] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? xoff + 16 : xoff, 0, 0);
     };
-    auto stash = [&](char *buf, const u32x4 &cw, const u32x4 &cx) {
-        const half8 hw = __builtin_bit_cast(half8, cw), hx = __builtin_bit_cast(half8, cx);
+    auto stash = [&](char *buf, const u32x4 &cw, const u32x4 (&cx)[2]) {
+        const half8 hw = __builtin_bit_cast(half8, cw);
+        const f32x4 x0 = act4<kF32>(cx, 0), x1 = act4<kF32>(cx, 1);
         float *fw = reinterpret_cast<float *>(buf), *fx = reinterpret_cast<float *>(buf + kLBuf);
 #pragma unroll
         for (int e = 0; e < 8; e++) {
             fw[(lt * 8 + e) * kLG + lr] = (float)hw[e];
-            fx[(lt * 8 + e) * kLG + lr] = (float)hx[e];
+            fx[(lt * 8 + e) * kLG + lr] = e < 4 ? x0[e] : x1[e - 4];
         }
     };
 
     const int64_t nstages = (k + kKS - 1) / kKS;
-    u32x4 cw, cx;
+    u32x4 cw, cx[2];
     fetch(0, cw, cx);
     stash(lds, cw, cx);
     fetch(kKS, cw, cx);
@@ -478,12 +532,13 @@ __global__ __launch_bounds__(256) void tinyblas_lanes(GemmTable g, int64_t k, co
 
 }  // namespace
 
-hipError_t launch_sgemm(GemmTable g, int64_t k, const uint16_t *a, int64_t n, bool aligned16,
+hipError_t launch_sgemm(GemmTable g, int64_t k, const void *a, int64_t n, bool aligned16, bool f32act,
                         hipStream_t stream)
 {
+    const int64_t esz = f32act ? 4 : 2;   // activation element bytes
     // few tiles: one block per 32 x 32 tile, its four instructions on four
     // waves (aligned operands, 32-row tile resources under 2^31 bytes)
-    if (aligned16 && (int64_t)kLT * k * 2 < ((int64_t)1 << 31)) {
+    if (aligned16 && (int64_t)kLT * k * esz < ((int64_t)1 << 31)) {
         const int64_t nct32 = (n + kLT - 1) / kLT;
         int64_t t32 = 0;
         for (int m = 0; m < g.count; m++) t32 += (g.rows[m] + kLT - 1) / kLT * nct32;
@@ -494,7 +549,11 @@ hipError_t launch_sgemm(GemmTable g, int64_t k, const uint16_t *a, int64_t n, bo
                 acc += (g.rows[m] + kLT - 1) / kLT * nct32;
             }
             g.tile0[g.count] = (int32_t)acc;
-            tinyblas_lanes<<<dim3((uint32_t)acc), dim3(256), 0, stream>>>(g, k, a, n, (int)nct32);
+            const dim3 grid((uint32_t)acc);
+            if (f32act)
+                tinyblas_lanes<true><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct32);
+            else
+                tinyblas_lanes<false><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct32);
             return hipGetLastError();
         }
     }
@@ -509,10 +568,18 @@ hipError_t launch_sgemm(GemmTable g, int64_t k, const uint16_t *a, int64_t n, bo
     const dim3 grid((uint32_t)tiles);
     // buffer offsets are 32-bit with bit 31 marking chunks past k: a tile of
     // kBN columns must stay under 2^31 bytes
-    if (aligned16 && (int64_t)kBN * k * 2 < ((int64_t)1 << 31))
-        tinyblas_mfma<true><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
-    else
-        tinyblas_mfma<false><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+    const bool buf = aligned16 && (int64_t)kBN * k * esz < ((int64_t)1 << 31);
+    if (f32act) {
+        if (buf)
+            tinyblas_mfma<true, true><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+        else
+            tinyblas_mfma<false, true><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+    } else {
+        if (buf)
+            tinyblas_mfma<true, false><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+        else
+            tinyblas_mfma<false, false><<<grid, dim3(256), 0, stream>>>(g, k, a, n, (int)nct);
+    }
     return hipGetLastError();
 }
 

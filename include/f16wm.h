@@ -146,6 +146,25 @@ int f16wm_mat_mul_multi(const f16wm_mat *mats, int32_t count, int64_t k, const u
                         void *stream);
 
 /*
+ * f16wm_mat_mul_f32 / f16wm_mat_mul_multi_f32: f16wm_mat_mul /
+ * f16wm_mat_mul_multi taking the activation block as f32 values x [n][k]
+ * (column c at x + c*k): each value is rounded to f16 exactly as f16wm_to_f16
+ * rounds it (same code) while the product stages it, so the result equals
+ * f16wm_to_f16 on the block followed by the f16 entry point, bit for bit, in
+ * one launch and without writing the rounded block out.  f16 page, Design
+ * notes ("Activation": the activation is rounded before any product) and
+ * Matrix products (mat_mul_par); bankML page "bankML/forward.rs", Advantages
+ * and efficiency (one rounded activation feeds Q, K and V, another gate and
+ * up).  x: 4-byte aligned; 16-byte alignment selects the vectorised kernels
+ * (the bits are the same).  Errors and the other arguments as for the f16
+ * entry points.
+ */
+int f16wm_mat_mul_f32(const uint16_t *w, int64_t rows, int64_t k, const float *x, int64_t n, float *out,
+                      void *stream);
+int f16wm_mat_mul_multi_f32(const f16wm_mat *mats, int32_t count, int64_t k, const float *x, int64_t n,
+                            void *stream);
+
+/*
  * f16wm_mat_mul_mfma: the same product and layout as f16wm_mat_mul computed on
  * the fp16 matrix cores (MFMA, f16 x f16 products, f32 accumulation).  An
  * approximate fast path for prefill micro-batches (bankML page

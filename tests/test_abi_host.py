@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
         "f16wm_to_f16", "f16wm_widen", "f16wm_get_rows", "f16wm_mat_vec", "f16wm_mat_vec_multi",
         "f16wm_mat_vec_f32", "f16wm_mat_vec_multi_f32", "f16wm_mat_mul", "f16wm_mat_mul_mfma",
         "f16wm_mat_mul_multi", "f16wm_mat_mul_mfma_multi", "f16wm_takes_sgemm", "f16wm_last_error",
-        "f16wm_version", "f16wm_mat_mul_out", "f16wm_kq", "f16wm_mad", "f16wm_scale"])
+        "f16wm_version", "f16wm_mat_mul_out", "f16wm_kq", "f16wm_mad", "f16wm_scale",
+        "f16wm_mat_mul_f32", "f16wm_mat_mul_multi_f32"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -117,6 +118,22 @@ def test_mat_mul_rejects_bad_arguments(L):
     assert "overlap" in _err(L.f16wm_mat_mul(P, 4, 8, P + 4096, 3, P + 4100, STREAM))
     assert "null" in _err(L.f16wm_mat_mul(P, 4, 8, None, 3, P + 8192, STREAM))
     assert "too large" in _err(L.f16wm_mat_mul(P, 1 << 21, 8, P, 1 << 21, P, STREAM))
+
+
+def test_f32_activation_products_reject_bad_arguments(L):
+    """f16wm_mat_mul_f32 / _multi_f32 check the f32 block as 4-byte elements:
+    alignment, null, overlap with the output over n*k*4 bytes; an empty
+    product returns 0 before any device call."""
+    assert "misaligned" in _err(L.f16wm_mat_mul_f32(P, 4, 8, P + 4098, 3, P + 8192, STREAM))
+    assert "null" in _err(L.f16wm_mat_mul_f32(P, 4, 8, None, 3, P + 8192, STREAM))
+    # x spans 3 * 8 * 4 = 96 bytes from P + 4096: an output at P + 4160 overlaps it
+    assert "overlap" in _err(L.f16wm_mat_mul_f32(P, 4, 8, P + 4096, 3, P + 4160, STREAM))
+    assert L.f16wm_mat_mul_f32(P, 0, 8, P + 4096, 3, P + 8192, STREAM) == 0
+    Mat = f16wm._Mat
+    mats = (Mat * 1)()
+    mats[0].w, mats[0].rows, mats[0].out = P, 4, P + (1 << 20)
+    assert "count" in _err(L.f16wm_mat_mul_multi_f32(mats, 0, 8, P + (1 << 21), 3, STREAM))
+    assert "misaligned" in _err(L.f16wm_mat_mul_multi_f32(mats, 1, 8, P + (1 << 21) + 2, 3, STREAM))
 
 
 def test_grouped_products_reject_bad_arguments(L):

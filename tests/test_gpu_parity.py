@@ -309,6 +309,45 @@ def test_f32_activation_multi(orc, shapes):
         assert_bits_equal(o.cpu().numpy(), orc.mat_vec(w, x16), "multi f32 matrix %d" % i)
 
 
+@pytest.mark.parametrize("rows,k,n,off", [
+    (576, 576, 512, 0),     # tinyBLAS order, one wave per instruction (few tiles)
+    (2048, 1024, 512, 0),   # tinyBLAS order, 64 x 64 blocks
+    (576, 1536, 7, 1),      # misaligned f32 block: guarded loads
+    (12, 1536, 5, 0),       # one ragged tile
+    (13, 1540, 3, 0),       # vec_dot order (rows % 4 != 0), k tail
+    (12, 33, 4, 1),         # vec_dot order (k % 8 != 0), misaligned
+])
+def test_f32_activation_products(orc, rows, k, n, off):
+    """mat_mul with an f32 block equals to_f16 then mat_mul, every bit (NaN
+    payloads included), in every kernel class; the smaller cases also equal
+    the oracle.  Each column carries the rounding's edge values."""
+    w = synth.random_f16((75, rows, k), (rows, k), 0.02)
+    x = np.stack([f32_column((76, rows, k, c), k) for c in range(n)])
+    W, X = up16(w), up32(x, off)
+    got = f16wm.mat_mul(W, X)
+    ref = f16wm.mat_mul(W, f16wm.to_f16(X))
+    assert np.array_equal(bits(got), bits(ref)), "f32 block vs to_f16 then mat_mul"
+    if rows * k * n <= 200_000_000:
+        want = orc.mat_mul(w, orc.to_f16(x))
+        assert_bits_equal(got.cpu().numpy(), want, "mat_mul f32 %dx%d n=%d off=%d" % (rows, k, n, off))
+
+
+@pytest.mark.parametrize("shapes,n", [
+    ([(576, 576), (192, 576), (192, 576)], 512),
+    ([(4096, 512), (1024, 512)], 512),
+    ([(12, 100), (13, 100), (16, 100)], 5),
+])
+def test_f32_activation_grouped_products(orc, shapes, n):
+    k = shapes[0][1]
+    ws = [synth.random_f16((77, i, r, k), (r, k), 0.02) for i, (r, _) in enumerate(shapes)]
+    x = np.stack([f32_column((78, c, k), k) for c in range(n)])
+    Ws, X = [up16(w) for w in ws], up32(x)
+    got = f16wm.mat_mul_multi(Ws, X)
+    ref = f16wm.mat_mul_multi(Ws, f16wm.to_f16(X))
+    for i in range(len(ws)):
+        assert np.array_equal(bits(got[i]), bits(ref[i])), "matrix %d" % i
+
+
 # ------------------------------------------------------ grouped products
 
 @pytest.mark.parametrize("shapes,n", [
