@@ -404,6 +404,17 @@ def test_degenerate_sizes(orc):
     f16wm.mat_mul(torch.zeros((4, 16), dtype=torch.float16, device=DEV),
                   torch.empty((0, 16), dtype=torch.float16, device=DEV))
     f16wm.to_f16(torch.empty(0, device=DEV))
+    # the same through the f32-block entry points (tinyBLAS order for 8 rows,
+    # vec_dot order for 13)
+    x = torch.empty((3, 0), dtype=torch.float32, device=DEV)
+    for r in (8, 13):
+        outf = torch.full((3, r), 7.0, device=DEV)
+        f16wm.mat_mul(torch.empty((r, 0), dtype=torch.float16, device=DEV), x, outf)
+        assert (bits(outf) == 0).all(), r
+    f16wm.mat_mul(torch.empty((0, 16), dtype=torch.float16, device=DEV),
+                  torch.zeros((2, 16), dtype=torch.float32, device=DEV))
+    f16wm.mat_mul(torch.zeros((4, 16), dtype=torch.float16, device=DEV),
+                  torch.empty((0, 16), dtype=torch.float32, device=DEV))
 
 
 def test_inf_and_nan_propagate_like_the_oracle(orc):
