@@ -40,6 +40,14 @@ class _Mat(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p), ("rows", ctypes.c_int64), ("out", ctypes.c_void_p)]
 
 
+class _Gemv(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("a", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("k", ctypes.c_int64), ("a_f32", ctypes.c_int32)]
+
+
+MAX_TABLE = 4096
+
+
 _lib = None
 
 
@@ -59,6 +67,7 @@ def lib() -> ctypes.CDLL:
         L.f16wm_mat_vec_multi.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, P]
         L.f16wm_mat_vec_f32.argtypes = [P, I64, I64, P, P, P]
         L.f16wm_mat_vec_multi_f32.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, P]
+        L.f16wm_mat_vec_table.argtypes = [ctypes.POINTER(_Gemv), I32, P]
         L.f16wm_mat_mul.argtypes = [P, I64, I64, P, I64, P, P]
         L.f16wm_mat_mul_mfma.argtypes = [P, I64, I64, P, I64, P, P]
         L.f16wm_mat_mul_multi.argtypes = [ctypes.POINTER(_Mat), I32, I64, P, I64, P]
@@ -71,7 +80,7 @@ def lib() -> ctypes.CDLL:
         L.f16wm_mad.argtypes = [P, P, P, I64, I64, P]
         L.f16wm_scale.argtypes = [P, P, I64, I64, P]
         for f in ("f16wm_to_f16", "f16wm_widen", "f16wm_get_rows", "f16wm_mat_vec", "f16wm_mat_vec_multi", "f16wm_mat_vec_f32",
-                  "f16wm_mat_vec_multi_f32", "f16wm_mat_mul", "f16wm_mat_mul_mfma", "f16wm_mat_mul_multi",
+                  "f16wm_mat_vec_multi_f32", "f16wm_mat_vec_table", "f16wm_mat_mul", "f16wm_mat_mul_mfma", "f16wm_mat_mul_multi",
                   "f16wm_mat_mul_mfma_multi", "f16wm_mat_mul_f32", "f16wm_mat_mul_multi_f32", "f16wm_takes_sgemm",
                   "f16wm_mat_mul_out", "f16wm_kq", "f16wm_mad", "f16wm_scale"):
             getattr(L, f).restype = ctypes.c_int
@@ -245,6 +254,56 @@ def mat_vec_multi(ws, a: torch.Tensor, outs=None) -> list:
     with torch.cuda.device(dev):
         _check(fn(mats, len(ws), k, a.data_ptr(), _stream(dev)))
     return outs
+
+
+class VecTable:
+    """A prepared f16wm_mat_vec_table call: the C descriptors of a fixed list
+    of independent one-column products, built once so that a decode loop (or
+    a HIP graph capture) pays only the library call.  The tensors must stay
+    alive and in place while the table is used."""
+
+    def __init__(self, prods):
+        prods = list(prods)
+        if len(prods) > MAX_TABLE:
+            raise ValueError("at most %d products" % MAX_TABLE)
+        arr = (_Gemv * max(1, len(prods)))()
+        self.outs = []
+        self.device = None
+        for i, item in enumerate(prods):
+            w, a = item[0], item[1]
+            out = item[2] if len(item) > 2 else None
+            rows, k = _wk(w)
+            f32 = _act(a, "a")
+            if a.numel() != k:
+                raise ValueError("product %d: the column must have k = %d elements" % (i, k))
+            if out is None:
+                out = torch.empty(rows, dtype=torch.float32, device=w.device)
+            _f32(out, "out")
+            if out.numel() != rows:
+                raise ValueError("product %d: out must have rows = %d elements" % (i, rows))
+            if self.device is None:
+                self.device = w.device
+            if w.device != self.device or a.device != self.device or out.device != self.device:
+                raise ValueError("every tensor of a table must be on one device")
+            arr[i] = _Gemv(w.data_ptr(), a.data_ptr(), out.data_ptr(), rows, k, 1 if f32 else 0)
+            self.outs.append(out)
+        self._arr, self._n = arr, len(prods)
+        self._keep = prods
+
+    def __call__(self):
+        """Launch every product (on the current stream); returns the outputs."""
+        if self._n:
+            with torch.cuda.device(self.device):
+                _check(lib().f16wm_mat_vec_table(self._arr, self._n, _stream(self.device)))
+        return self.outs
+
+
+def mat_vec_table(prods) -> list:
+    """Independent one-column products, each (w, a) or (w, a, out): W [rows, k]
+    f16 times its own column a ([k] f16, or float32 rounded inside the launch),
+    out [rows] f32, in as few launches as the library can (f16wm_mat_vec_table).
+    Returns the outputs.  For repeated calls build a VecTable once."""
+    return VecTable(prods)()
 
 
 def _mm(fn, w, a, out, fn32=None):

@@ -9,8 +9,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <string>
+#include <vector>
 
 #include "kernels.h"
 
@@ -402,6 +404,89 @@ int f16wm_mat_mul_out(const uint16_t *w, int64_t rows, int64_t k, const uint16_t
     if (k > 0 && !a) return fail(F16WM_EINVAL, "%s: null activation", fn);
     // one column: the vec_dot order of f16wm_mat_vec
     return mat_vec_impl(fn, w, rows, k, a ? a + off : a, false, out, stream);
+}
+
+int f16wm_mat_vec_table(const f16wm_gemv *prods, int32_t count, void *stream)
+{
+    const char *fn = "f16wm_mat_vec_table";
+    if (count < 0 || count > F16WM_MAX_TABLE)
+        return fail(F16WM_EINVAL, "%s: count %d outside 0..%d", fn, (int)count, F16WM_MAX_TABLE);
+    if (count == 0) return ok();
+    if (!prods) return fail(F16WM_EINVAL, "%s: null table", fn);
+    // Every product as f16wm_mat_vec checks it; then outputs pairwise
+    // disjoint, and disjoint from every weight and column (sorted sweep).
+    std::vector<Span> outs, ins;
+    outs.reserve(count);
+    ins.reserve(2 * (size_t)count);
+    for (int p = 0; p < count; p++) {
+        const f16wm_gemv &g = prods[p];
+        char name[64];
+        snprintf(name, sizeof name, "%s[%d]", fn, p);
+        if (g.a_f32 != 0 && g.a_f32 != 1) return fail(F16WM_EINVAL, "%s: a_f32 is %d, not 0 or 1", name, (int)g.a_f32);
+        const int esz = g.a_f32 ? 4 : 2;
+        int64_t we, ae, oe;
+        if (int rc = check_product(name, g.w, g.rows, g.k, g.a, esz, 1, g.out, &we, &ae, &oe)) return rc;
+        if (oe > 0) outs.push_back(span(g.out, oe * 4));
+        if (oe > 0 && we > 0) ins.push_back(span(g.w, we * 2));
+        if (oe > 0 && ae > 0) ins.push_back(span(g.a, ae * esz));
+    }
+    std::sort(outs.begin(), outs.end(), [](const Span &x, const Span &y) { return x.lo < y.lo; });
+    for (size_t i = 1; i < outs.size(); i++)
+        if (outs[i].lo < outs[i - 1].hi) return fail(F16WM_EINVAL, "%s: two outputs overlap", fn);
+    for (const Span &in : ins) {
+        // the output with the largest start below the input's end is the only
+        // one that can overlap it (outputs are disjoint and sorted)
+        auto it = std::lower_bound(outs.begin(), outs.end(), in.hi,
+                                   [](const Span &o, uintptr_t hi) { return o.lo < hi; });
+        if (it != outs.begin() && std::prev(it)->hi > in.lo)
+            return fail(F16WM_EINVAL, "%s: an output overlaps a weight or column", fn);
+    }
+    if (outs.empty()) return ok();
+    if (int rc = check_device(fn)) return rc;
+
+    // Kernel classes: [direct? 1 : 0][f32 column? 1 : 0]; products that take
+    // no vectorised kernel launch one by one.
+    std::vector<int> cls[2][2];
+    for (int p = 0; p < count; p++) {
+        const f16wm_gemv &g = prods[p];
+        if (g.rows == 0) continue;
+        const bool vec8 = g.k % 8 == 0 && aligned(g.w, 16) && aligned(g.a, 16) && g.rows <= 0x7fffffff &&
+                          16 * 2 * g.k + 65536 <= 0x7fff0000;
+        if (!vec8) {
+            f16wm::RowTable t = {};
+            t.count = 1;
+            t.w[0] = g.w;
+            t.out[0] = g.out;
+            t.row0[1] = g.rows;
+            const bool v8 = g.k % 8 == 0 && aligned(g.w, 16) && aligned(g.a, 16);
+            const hipError_t e = f16wm::launch_vec_dot(t, g.k, g.a, g.a_f32 != 0, 1, v8, (hipStream_t)stream);
+            if (e != hipSuccess) return launched(fn, e);
+            continue;
+        }
+        cls[g.k <= f16wm::kDirectMaxKTable ? 1 : 0][g.a_f32 ? 1 : 0].push_back(p);
+    }
+    for (int d = 0; d < 2; d++)
+        for (int f = 0; f < 2; f++) {
+            std::vector<int> &v = cls[d][f];
+            // longest rows first, so the blocks that take longest start first
+            std::stable_sort(v.begin(), v.end(), [&](int x, int y) { return prods[x].k > prods[y].k; });
+            for (size_t c0 = 0; c0 < v.size(); c0 += f16wm::kTableChunk) {
+                f16wm::ProdTable t = {};
+                const size_t c1 = std::min(v.size(), c0 + (size_t)f16wm::kTableChunk);
+                for (size_t i = c0; i < c1; i++) {
+                    const f16wm_gemv &g = prods[v[i]];
+                    t.w[t.count] = g.w;
+                    t.a[t.count] = g.a;
+                    t.out[t.count] = g.out;
+                    t.rows[t.count] = (int32_t)g.rows;
+                    t.k[t.count] = (int32_t)g.k;
+                    t.count++;
+                }
+                const hipError_t e = f16wm::launch_vec_dot_table(t, d == 1, f == 1, (hipStream_t)stream);
+                if (e != hipSuccess) return launched(fn, e);
+            }
+        }
+    return ok();
 }
 
 int f16wm_kq(const uint16_t *kc, int64_t n_kv, int64_t n_kv_head, int64_t d, const uint16_t *q, int64_t n_head,

@@ -33,6 +33,23 @@ struct GemmTable {
     int32_t count;
 };
 
+// Independent one-column products, each with its own weight (rows[p] x
+// k[p] f16), column a[p] (k[p] values, all f16 or all f32 in one table) and
+// output out[p] (rows[p] f32).  tile0[p] is the first row tile of product p
+// (filled by the launcher for its tile height; tile0[count] is the total).
+// kTableChunk products fit in the 4 KB a kernel's arguments may take.
+constexpr int kTableChunk = 96;
+struct ProdTable {
+    const uint16_t *w[kTableChunk];
+    const void *a[kTableChunk];
+    float *out[kTableChunk];
+    int32_t rows[kTableChunk];
+    int32_t k[kTableChunk];
+    int32_t tile0[kTableChunk + 1];
+    int32_t count;
+};
+static_assert(sizeof(ProdTable) <= 4096, "kernel arguments stay within 4 KB");
+
 // The output tile `t` of a grouped product with `nct` column tiles: its
 // matrix, row tile and column tile.
 __device__ __forceinline__ void gemm_tile(const GemmTable &g, int t, int nct, int &m, int &rt, int &ct)
@@ -71,6 +88,17 @@ hipError_t launch_to_f16(const float *x, uint16_t *y, int64_t count, hipStream_t
 // and a.
 hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32act, int64_t ncols,
                           bool vec8, hipStream_t stream);
+
+// vec_dot order for every product of t in one launch.  Every product has
+// k % 8 == 0, 16-byte aligned w and a, rows < 2^31, and 16 * 2 * k + 64 KB
+// under 2^31 bytes; direct: every k <= kDirectMaxKTable (rows in registers),
+// else rows staged in LDS.  f32act: every column is f32, rounded in the
+// kernel exactly as launch_to_f16 rounds it.  The launcher fills tile0 and
+// fails (hipErrorInvalidConfiguration) past 2^31 - 1 row tiles.
+constexpr int64_t kDirectMaxKTable = 640;
+constexpr int kTableRowsDirect = 16;   // rows per block, direct kernel
+constexpr int kTableRowsLds = 16;      // rows per block, LDS kernel
+hipError_t launch_vec_dot_table(ProdTable t, bool direct, bool f32act, hipStream_t stream);
 
 // tinyBLAS order for every matrix of g (rows % 4 == 0, k % 8 == 0, n >= 2
 // checked by the caller).  aligned16: every w and a are 16-byte aligned.  The

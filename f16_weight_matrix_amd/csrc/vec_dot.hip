@@ -1,13 +1,18 @@
 // vec_dot order on gfx950: GEMV (one column), grouped GEMV, and the fallback
 // product for shapes that do not take the tinyBLAS path.
 //
-// bankML f16 page, Design notes ("vec_dot"): every output element is four
-// 8-lane f32 accumulators fed by FMAs over 32-element steps (accumulator j,
-// lane l takes elements 32t + 8j + l, ascending t), reduced (a0+a2)+(a1+a3) lane
-// by lane, then low four lanes + high four, then two horizontal adds of
-// adjacent pairs; the k % 32 tail is added to that f32 in binary64 and the
-// double is rounded to f32.  Matrix products (mat_vec_par,
-// mat_vec_multi_par): out[r] = vec_dot(W[r], a), several matrices in one pass.
+// The order (bankML page "bankML/f16.rs -- F16 weights, multiplied as the
+// shipped ggml b11192 multiplies them", Design notes, "vec_dot"; Matrix
+// products for mat_vec_par / mat_vec_multi_par):
+//  - chains: element i < 32 * floor(k / 32) goes to chain c = i % 32, and
+//    every chain is one sequential f32 FMA chain from +0 in ascending i;
+//  - tree: chains c and c + 16 are added, then those sums pairwise by bit 8
+//    of c, then by bit 4, then two rounds of neighbour sums (bit 1, then
+//    bit 2), leaving one f32;
+//  - tail: the k % 32 last products are added to that f32 one by one in
+//    binary64 and the double is rounded to f32 once;
+//  - out[r] = that value for row r of W against the column, for one or
+//    several matrices per launch.
 //
 // Each of the 32 chains of an element is a sequential FMA chain, so one chain
 // lives in one GPU lane for the whole row; the tree is a fixed sequence of
@@ -175,8 +180,14 @@ struct Depth {
     static constexpr int D = 4;
 };
 
+//
+// lds_tile is one block's work: rows r0 .. r0 + R - 1 of the matrix wm
+// (rows_m x k) against the column a, results to out (out[r] for row r).
+// The GEMV kernels below call it for a row tile of a RowTable matrix, or of
+// one product of a ProdTable.
 template <int LPR, bool kF32, bool kWhole>
-__global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const void *__restrict__ a_all)
+__device__ __forceinline__ void lds_tile(const uint16_t *__restrict__ wm, int64_t rows_m, int64_t r0, int64_t k,
+                                         const void *__restrict__ a, float *__restrict__ out)
 {
     typedef LdsCfg<LPR> C;
     typedef typename Halves<C::CPL>::T HT;
@@ -187,18 +198,8 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const 
     unsigned char *actl = lds + 2 * BUF;                 // whole column (kWhole)
 
     const int tid = threadIdx.x;
-    const int64_t col = blockIdx.y;
-    const void *a = static_cast<const char *>(a_all) + col * k * ESZ;
-
-    // This block's matrix and row tile.
-    int m = 0;
-#pragma unroll
-    for (int i = 1; i < F16WM_MAX_MULTI; i++)
-        if (i < t.count && (int64_t)blockIdx.x >= t.tile0[i]) m = i;
-    const int64_t rows_m = t.row0[m + 1] - t.row0[m];
-    const int64_t r0 = ((int64_t)blockIdx.x - t.tile0[m]) * C::R;
     const int64_t vrows = rows_m - r0 < C::R ? rows_m - r0 : C::R;
-    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(t.w[m] + r0 * k, vrows * k * 2);
+    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wm + r0 * k, vrows * k * 2);
     const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(a, k * ESZ);
 
     // Byte offsets of this thread's stage units in stage 0: unit f = row
@@ -313,10 +314,50 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const 
     float v = vec_dot_tree<C::CPL>(acc);
     const int64_t r = r0 + rho;
     if (j == 0 && r < rows_m) {
-        const uint16_t *wrow = t.w[m] + r * k;
+        const uint16_t *wrow = wm + r * k;
         if (k & 31) v = add_tail<kF32>(v, wrow, a, nsteps * 32, k);
-        t.out[m][col * rows_m + r] = v;
+        out[r] = v;
     }
+}
+
+// Row tile blockIdx.x - tile0[m] of matrix m of the RowTable, against column
+// blockIdx.y.
+template <int LPR, bool kF32, bool kWhole>
+__global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const void *__restrict__ a_all)
+{
+    constexpr int ESZ = kF32 ? 4 : 2;
+    const int64_t col = blockIdx.y;
+    int m = 0;
+#pragma unroll
+    for (int i = 1; i < F16WM_MAX_MULTI; i++)
+        if (i < t.count && (int64_t)blockIdx.x >= t.tile0[i]) m = i;
+    const int64_t rows_m = t.row0[m + 1] - t.row0[m];
+    const int64_t r0 = ((int64_t)blockIdx.x - t.tile0[m]) * LdsCfg<LPR>::R;
+    lds_tile<LPR, kF32, kWhole>(t.w[m], rows_m, r0, k, static_cast<const char *>(a_all) + col * k * ESZ,
+                                t.out[m] + col * rows_m);
+}
+
+// The product of a ProdTable that block b belongs to: the last p with
+// tile0[p] <= b (binary search over the table in the kernel arguments).
+__device__ __forceinline__ int table_product(const ProdTable &t, int b)
+{
+    int lo = 0, hi = t.count - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (t.tile0[mid] <= b) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Row tile blockIdx.x - tile0[p] of product p of the table (each product
+// has its own weight, column, k and output).
+template <int LPR, bool kF32, bool kWhole>
+__global__ __launch_bounds__(256) void vec_dot_lds_table(ProdTable t)
+{
+    const int p = table_product(t, (int)blockIdx.x);
+    const int64_t r0 = (int64_t)((int)blockIdx.x - t.tile0[p]) * LdsCfg<LPR>::R;
+    lds_tile<LPR, kF32, kWhole>(t.w[p], t.rows[p], r0, t.k[p], t.a[p], t.out[p]);
 }
 
 // Short rows (k <= kDirectMaxK, k % 8 == 0, 16-byte aligned): no staging.
@@ -329,21 +370,19 @@ __global__ __launch_bounds__(256) void vec_dot_lds(RowTable t, int64_t k, const 
 // few round trips long.
 constexpr int kDirectMaxK = 640;              // 20 steps of 32
 constexpr int kDirectRows = 16;               // rows per one-wave block
+static_assert(kDirectMaxK == kDirectMaxKTable && kDirectRows == kTableRowsDirect, "table launcher's view");
+static_assert(LdsCfg<16>::R == kTableRowsLds, "table launcher's view");
 
+// direct_rows: this lane's row wrow (valid lanes) against the column a, the
+// result to *dst; the block's 64 threads hold 16 rows (one per lane quad) and
+// share `actl` (kDirectMaxK halves of LDS) for the rounded column.
 template <bool kF32>
-__global__ __launch_bounds__(64) void vec_dot_direct(RowTable t, int64_t k, const void *__restrict__ a_all)
+__device__ __forceinline__ void direct_rows(unsigned char *actl, const uint16_t *__restrict__ wrow, bool valid,
+                                            int64_t k, const void *__restrict__ a, float *__restrict__ dst)
 {
     constexpr int MAXS = kDirectMaxK / 32;
-    __shared__ __attribute__((aligned(16))) unsigned char actl[kDirectMaxK * 2];
     const int tid = threadIdx.x;
-    const int64_t col = blockIdx.y;
-    const void *a = static_cast<const char *>(a_all) + col * k * (kF32 ? 4 : 2);
     const int j = tid & 3;
-    const int64_t g = (int64_t)blockIdx.x * kDirectRows + (tid >> 2);
-    const bool valid = g < t.row0[t.count];
-    const int m = find_matrix(t, valid ? g : 0);
-    const int64_t r = valid ? g - t.row0[m] : 0;
-    const uint16_t *wrow = t.w[m] + r * k;
     const int nsteps = (int)(k >> 5);
 
     u32x4 wv[MAXS];
@@ -372,9 +411,36 @@ __global__ __launch_bounds__(64) void vec_dot_direct(RowTable t, int64_t k, cons
     float v = vec_dot_tree<8>(acc);
     if (valid && j == 0) {
         if (k & 31) v = add_tail<kF32>(v, wrow, a, (int64_t)nsteps * 32, k);
-        const int64_t rows_m = t.row0[m + 1] - t.row0[m];
-        t.out[m][col * rows_m + r] = v;
+        *dst = v;
     }
+}
+
+// Global rows 16 blockIdx.x .. + 15 of the RowTable (rows of several
+// matrices may share a block), column blockIdx.y.
+template <bool kF32>
+__global__ __launch_bounds__(64) void vec_dot_direct(RowTable t, int64_t k, const void *__restrict__ a_all)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char actl[kDirectMaxK * 2];
+    const int64_t col = blockIdx.y;
+    const void *a = static_cast<const char *>(a_all) + col * k * (kF32 ? 4 : 2);
+    const int64_t g = (int64_t)blockIdx.x * kDirectRows + (threadIdx.x >> 2);
+    const bool valid = g < t.row0[t.count];
+    const int m = find_matrix(t, valid ? g : 0);
+    const int64_t r = valid ? g - t.row0[m] : 0;
+    const int64_t rows_m = t.row0[m + 1] - t.row0[m];
+    direct_rows<kF32>(actl, t.w[m] + r * k, valid, k, a, t.out[m] + col * rows_m + r);
+}
+
+// Rows 16 (blockIdx.x - tile0[p]) .. + 15 of product p of the table.
+template <bool kF32>
+__global__ __launch_bounds__(64) void vec_dot_direct_table(ProdTable t)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char actl[kDirectMaxK * 2];
+    const int p = table_product(t, (int)blockIdx.x);
+    const int64_t k = t.k[p];
+    const int64_t r = (int64_t)((int)blockIdx.x - t.tile0[p]) * kDirectRows + (threadIdx.x >> 2);
+    const bool valid = r < t.rows[p];
+    direct_rows<kF32>(actl, t.w[p] + (valid ? r : 0) * k, valid, k, t.a[p], t.out[p] + r);
 }
 
 constexpr int kV1Rows = 8;    // rows per 256-thread block, 32 lanes per row
@@ -442,7 +508,43 @@ void launch_lds(dim3 grid, hipStream_t stream, const RowTable &t, int64_t k, con
     }
 }
 
+template <bool kF32, bool kWhole>
+hipError_t launch_lds_table(const ProdTable &t, int64_t maxk, hipStream_t stream)
+{
+    typedef LdsCfg<16> C;
+    const int max_shm = kWhole ? 2 * C::WBYTES + (int)kWholeMaxK * 2 : 2 * C::BUFB;
+    const size_t shm = kWhole ? 2 * C::WBYTES + (size_t)maxk * 2 : 2 * C::BUFB;
+    allow_dynamic_lds(reinterpret_cast<const void *>(vec_dot_lds_table<16, kF32, kWhole>), max_shm);
+    vec_dot_lds_table<16, kF32, kWhole><<<dim3((uint32_t)t.tile0[t.count]), dim3(256), shm, stream>>>(t);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_vec_dot_table(ProdTable t, bool direct, bool f32act, hipStream_t stream)
+{
+    const int per = direct ? kDirectRows : LdsCfg<16>::R;
+    int64_t tiles = 0, maxk = 0;
+    for (int p = 0; p < t.count; p++) {
+        t.tile0[p] = (int32_t)tiles;
+        tiles += ((int64_t)t.rows[p] + per - 1) / per;
+        if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;   // grid.x limit
+        if (t.k[p] > maxk) maxk = t.k[p];
+    }
+    t.tile0[t.count] = (int32_t)tiles;
+    if (tiles == 0) return hipSuccess;
+    if (direct) {
+        if (maxk > kDirectMaxK) return hipErrorInvalidValue;
+        if (f32act)
+            vec_dot_direct_table<true><<<dim3((uint32_t)tiles), dim3(64), 0, stream>>>(t);
+        else
+            vec_dot_direct_table<false><<<dim3((uint32_t)tiles), dim3(64), 0, stream>>>(t);
+        return hipGetLastError();
+    }
+    if (maxk <= kWholeMaxK)
+        return f32act ? launch_lds_table<true, true>(t, maxk, stream) : launch_lds_table<false, true>(t, maxk, stream);
+    return f32act ? launch_lds_table<true, false>(t, maxk, stream) : launch_lds_table<false, false>(t, maxk, stream);
+}
 
 hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32act, int64_t ncols,
                           bool vec8, hipStream_t stream)

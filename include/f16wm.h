@@ -13,7 +13,7 @@
  * Conventions for every entry point below:
  *  - All array pointers are DEVICE pointers owned by the caller.  The library
  *    reads/writes them in stream order during the call's kernels and keeps no
- *    reference afterwards; it never frees them and allocates no memory.
+ *    reference afterwards; it never frees them and allocates no device memory.
  *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls are
  *    asynchronous: they enqueue kernels and return without synchronising.
  *  - Validation happens on the host before any launch.  On failure nothing is
@@ -101,6 +101,44 @@ int f16wm_mat_vec(const uint16_t *w, int64_t rows, int64_t k, const uint16_t *a,
  */
 int f16wm_mat_vec_multi(const f16wm_mat *mats, int32_t count, int64_t k, const uint16_t *a,
                         void *stream);
+
+/* One product of a table launch (f16wm_mat_vec_table): out = W x column. */
+typedef struct {
+    const uint16_t *w;   /* rows x k f16, row-major (k contiguous), device */
+    const void *a;       /* the column, k values, device: f16 bit patterns (a_f32 = 0), or f32 (a_f32 = 1) */
+    float *out;          /* rows f32, device */
+    int64_t rows;
+    int64_t k;
+    int32_t a_f32;       /* 0 or 1 */
+} f16wm_gemv;
+
+#define F16WM_MAX_TABLE 4096   /* products per f16wm_mat_vec_table call */
+
+/*
+ * f16wm_mat_vec_table: `count` (0..F16WM_MAX_TABLE) independent one-column
+ * products, prods[p].out[r] = vec_dot(W_p[r], column_p) for r < rows_p, each
+ * with its own weight, k, column and output; an f32 column is rounded to f16
+ * as f16wm_to_f16 rounds it, inside the launch.  Every element is the
+ * f16wm_mat_vec (or f16wm_mat_vec_f32) result bit for bit: the grouping
+ * decides only which block computes a row, never its order.
+ * f16 page, Matrix products (mat_vec_par per row; mat_vec_multi_par: several
+ * matrices in one pass) and Advantages and efficiency (grouped matrices are
+ * handed to the pool as one job instead of one per matrix); here the job
+ * table generalises the grouping to products that share nothing, such as
+ * every product of a decode step whose columns are already known, or the
+ * same layer for several sequences.
+ * Launches: products with k % 8 == 0 and 16-byte aligned w and a run in one
+ * launch per kernel class (k <= 640: rows in registers; longer rows: staged
+ * in LDS; f16 or f32 columns) and per 96 products of a class, longest k
+ * first; any other product takes its own f16wm_mat_vec launch.  Nothing runs
+ * in between, so the products may not depend on each other: every output
+ * must be disjoint from every other output and from every weight and column
+ * (F16WM_EINVAL); columns and weights may be shared.  `prods` is a HOST
+ * array read during the call.  rows_p = 0 is a no-op for that product and
+ * k_p = 0 writes +0.0.  Errors as for f16wm_mat_vec, reported with the
+ * product's index; nothing is launched if any product is invalid.
+ */
+int f16wm_mat_vec_table(const f16wm_gemv *prods, int32_t count, void *stream);
 
 /*
  * f16wm_mat_vec_f32 / f16wm_mat_vec_multi_f32: the same products taking the

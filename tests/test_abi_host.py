@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
         "f16wm_mat_vec_f32", "f16wm_mat_vec_multi_f32", "f16wm_mat_mul", "f16wm_mat_mul_mfma",
         "f16wm_mat_mul_multi", "f16wm_mat_mul_mfma_multi", "f16wm_takes_sgemm", "f16wm_last_error",
         "f16wm_version", "f16wm_mat_mul_out", "f16wm_kq", "f16wm_mad", "f16wm_scale",
-        "f16wm_mat_mul_f32", "f16wm_mat_mul_multi_f32"])
+        "f16wm_mat_mul_f32", "f16wm_mat_mul_multi_f32", "f16wm_mat_vec_table"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -178,6 +178,47 @@ def test_mat_vec_multi_rejects_bad_arguments(L):
     mats[1].out = P + (1 << 20) + 4096
     mats[1].rows = -1
     assert "negative" in _err(L.f16wm_mat_vec_multi(mats, 2, 8, P + (1 << 21), STREAM))
+
+
+def _table(items):
+    G = f16wm._Gemv
+    arr = (G * max(1, len(items)))()
+    for i, (w, a, out, rows, k, f32) in enumerate(items):
+        arr[i] = G(w, a, out, rows, k, f32)
+    return arr
+
+
+def test_mat_vec_table_rejects_bad_arguments(L):
+    """f16wm_mat_vec_table validates every product as f16wm_mat_vec does and
+    refuses outputs that overlap another output, a weight or a column, all
+    before any device call (the pointers here are never dereferenced)."""
+    good = (P, P + 4096, P + 8192, 4, 8, 0)
+    t = _table([good])
+    assert "count" in _err(L.f16wm_mat_vec_table(t, -1, STREAM))
+    assert "count" in _err(L.f16wm_mat_vec_table(t, f16wm.MAX_TABLE + 1, STREAM))
+    assert "null table" in _err(L.f16wm_mat_vec_table(None, 2, STREAM))
+    assert L.f16wm_mat_vec_table(None, 0, STREAM) == 0
+    assert "a_f32" in _err(L.f16wm_mat_vec_table(_table([(P, P + 4096, P + 8192, 4, 8, 2)]), 1, STREAM))
+    msg = _err(L.f16wm_mat_vec_table(_table([good, (P, P + 4096, P + 8192, -4, 8, 0)]), 2, STREAM))
+    assert "[1]" in msg and "negative" in msg
+    assert "null" in _err(L.f16wm_mat_vec_table(_table([(P, None, P + 8192, 4, 8, 0)]), 1, STREAM))
+    assert "misaligned" in _err(L.f16wm_mat_vec_table(_table([(P, P + 4098, P + 8192, 4, 8, 1)]), 1, STREAM))
+    # two outputs overlap: 4 floats at P + 8192 and at P + 8200
+    two = [good, (P + 65536, P + 4096, P + 8200, 4, 8, 0)]
+    assert "two outputs" in _err(L.f16wm_mat_vec_table(_table(two), 2, STREAM))
+    # an output overlaps another product's weight (4 x 8 halves at P + 65536)
+    cross = [good, (P + 65536, P + 4096, P + 12288, 4, 8, 0), (P + 16384, P + 4096, P + 65540, 1, 8, 0)]
+    assert "weight or column" in _err(L.f16wm_mat_vec_table(_table(cross), 3, STREAM))
+    # ... or another product's f32 column (8 floats at P + 4096)
+    col = [(P, P + 4096, P + 8192, 4, 8, 1), (P + 65536, P + 12288, P + 4124, 1, 8, 0)]
+    assert "weight or column" in _err(L.f16wm_mat_vec_table(_table(col), 2, STREAM))
+    # shared weights and columns are fine, and so are empty products
+    shared = [(P, P + 4096, P + 8192, 4, 8, 0), (P, P + 4096, P + 12288, 4, 8, 0), (P, P + 4096, P + 8192, 0, 8, 0)]
+    assert L.f16wm_mat_vec_table(_table(shared[2:]), 1, STREAM) == 0
+    import torch
+    if not torch.cuda.is_available():
+        rc = L.f16wm_mat_vec_table(_table(shared), 3, STREAM)
+        assert rc == f16wm.F16WM_ENODEV, (rc, f16wm.last_error())
 
 
 def test_next_rows_reject_bad_arguments(L):

@@ -4,10 +4,13 @@ element, on the same seeded inputs.
 Exact paths (to_f16, vec_dot, tinyBLAS) must be bit-identical to the oracle
 (NaN compared as "is NaN").  The MFMA fast path must stay within
 max |y - ref| / sum_i |w_i a_i| <= 2e-3 of the binary64 reference.
-Full-size products are checked completely where the oracle is fast enough
-(every n = 1 product, layer 0 of the 135M prefill) and on sampled elements
-otherwise (the oracle computes each sampled element with the full shape's
-order).
+Every exact product is checked completely, the full-size ones included
+(every n = 1 product of both decode steps, every n = 512 product of the
+135M layer 0 and of the 8B set, the oracle running on the host's cores).  The
+MFMA path is checked on samples: at least 16 elements in every 64 x 64 block
+of the output (every tile of every launch shape is a union of such blocks),
+against the 2e-3 gate, a bound derived from f32 accumulation, and the plain
+relative error on elements that are not near zero.
 """
 import concurrent.futures as cf
 import os
@@ -27,6 +30,19 @@ import f16_weight_matrix_amd as f16wm  # noqa: E402
 
 DEV = torch.device("cuda:0")
 MFMA_TOL = 2e-3
+
+
+def host_threads() -> int:
+    """Oracle threads: the cores this process may run on, at most 16 (one
+    GPU's share of a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+HOST_T = host_threads()
 
 
 def say(*a):
@@ -309,43 +325,72 @@ def test_f32_activation_multi(orc, shapes):
         assert_bits_equal(o.cpu().numpy(), orc.mat_vec(w, x16), "multi f32 matrix %d" % i)
 
 
+# Exact tinyBLAS-order kernels by launch size: a launch of at most 1024
+# 32 x 32 output tiles runs one tile per block (tinyblas_lanes); a larger one
+# runs 64 x 64 blocks (tinyblas_mfma) with buffer loads when the operands are
+# 16-byte aligned and guarded loads otherwise.  k % 64 != 0 leaves a partial
+# last stage, whose chunks past k read zero.
 @pytest.mark.parametrize("rows,k,n,off", [
-    (576, 576, 512, 0),     # tinyBLAS order, one wave per instruction (few tiles)
-    (2048, 1024, 512, 0),   # tinyBLAS order, 64 x 64 blocks
-    (576, 1536, 7, 1),      # misaligned f32 block: guarded loads
+    (576, 576, 512, 0),     # 288 tiles: tinyblas_lanes
+    (2048, 1024, 512, 0),   # exactly 1024 tiles: still tinyblas_lanes
+    (2080, 1024, 512, 0),   # 1040 tiles: 64 x 64 blocks, f32 block through buffer loads
+    (2080, 1000, 512, 0),   # 1040 tiles, k % 64 = 40: a partial last stage
+    (2080, 1000, 500, 0),   # ragged last column block too
+    (2080, 1000, 512, 1),   # misaligned f32 block: guarded loads
+    (576, 1536, 7, 1),      # misaligned f32 block, few tiles: guarded loads
     (12, 1536, 5, 0),       # one ragged tile
     (13, 1540, 3, 0),       # vec_dot order (rows % 4 != 0), k tail
     (12, 33, 4, 1),         # vec_dot order (k % 8 != 0), misaligned
 ])
 def test_f32_activation_products(orc, rows, k, n, off):
-    """mat_mul with an f32 block equals to_f16 then mat_mul, every bit (NaN
-    payloads included), in every kernel class; the smaller cases also equal
-    the oracle.  Each column carries the rounding's edge values."""
+    """mat_mul with an f32 block equals the oracle (to_f16, then the shape's
+    order) on every element, and equals to_f16 then mat_mul on the GPU bit
+    for bit (NaN payloads included), in every kernel class.  Each column
+    carries the rounding's edge values."""
     w = synth.random_f16((75, rows, k), (rows, k), 0.02)
     x = np.stack([f32_column((76, rows, k, c), k) for c in range(n)])
     W, X = up16(w), up32(x, off)
     got = f16wm.mat_mul(W, X)
     ref = f16wm.mat_mul(W, f16wm.to_f16(X))
     assert np.array_equal(bits(got), bits(ref)), "f32 block vs to_f16 then mat_mul"
-    if rows * k * n <= 200_000_000:
-        want = orc.mat_mul(w, orc.to_f16(x))
-        assert_bits_equal(got.cpu().numpy(), want, "mat_mul f32 %dx%d n=%d off=%d" % (rows, k, n, off))
+    want = orc.mat_mul(w, orc.to_f16(x), threads=HOST_T)
+    assert_bits_equal(got.cpu().numpy(), want, "mat_mul f32 %dx%d n=%d off=%d" % (rows, k, n, off))
+
+
+@pytest.mark.parametrize("rows,k,n,woff,aoff", [
+    (2048, 1024, 512, 0, 0), (2080, 1024, 512, 0, 0), (2080, 1000, 512, 0, 0), (2080, 1000, 500, 0, 0),
+    (2080, 1000, 512, 1, 0), (2080, 1000, 512, 0, 3), (14336, 4096, 96, 0, 0)])
+def test_many_tile_exact_products(orc, rows, k, n, woff, aoff):
+    """f16 activation blocks on both sides of the 1024-tile switch, with a
+    partial last k stage, ragged column blocks, and misaligned operands
+    (guarded loads), every element against the oracle."""
+    w = synth.random_f16((79, rows, k), (rows, k), 0.02)
+    a = synth.random_f16((80, n, k), (n, k))
+    got = f16wm.mat_mul(up16(w, woff), up16(a, aoff)).cpu().numpy()
+    assert_bits_equal(got, orc.mat_mul(w, a, threads=HOST_T), "mat_mul %dx%d n=%d offs=%d,%d"
+                      % (rows, k, n, woff, aoff))
 
 
 @pytest.mark.parametrize("shapes,n", [
     ([(576, 576), (192, 576), (192, 576)], 512),
-    ([(4096, 512), (1024, 512)], 512),
+    ([(4096, 512), (1024, 512)], 512),                # 2560 tiles: 64 x 64 blocks, f32 block
+    ([(4096, 1000), (1024, 1000), (1024, 1000)], 512),  # partial last stage in a grouped launch
     ([(12, 100), (13, 100), (16, 100)], 5),
 ])
 def test_f32_activation_grouped_products(orc, shapes, n):
+    """Grouped exact products with an f32 block: every element against the
+    oracle, and bit-equal to to_f16 then the f16 grouped product."""
     k = shapes[0][1]
     ws = [synth.random_f16((77, i, r, k), (r, k), 0.02) for i, (r, _) in enumerate(shapes)]
     x = np.stack([f32_column((78, c, k), k) for c in range(n)])
+    x16 = orc.to_f16(x)
     Ws, X = [up16(w) for w in ws], up32(x)
     got = f16wm.mat_mul_multi(Ws, X)
     ref = f16wm.mat_mul_multi(Ws, f16wm.to_f16(X))
     for i in range(len(ws)):
         assert np.array_equal(bits(got[i]), bits(ref[i])), "matrix %d" % i
+        assert_bits_equal(got[i].cpu().numpy(), orc.mat_mul(ws[i], x16, threads=HOST_T),
+                          "grouped f32 matrix %d %s n=%d" % (i, shapes[i], n))
 
 
 # ------------------------------------------------------ grouped products
@@ -376,12 +421,9 @@ def test_grouped_mfma_products(orc, shapes, n):
     ws = [synth.random_f16((93, i, r, k), (r, k), 0.02) for i, (r, _) in enumerate(shapes)]
     a = synth.random_f16((94, k, n), (n, k))
     outs = f16wm.mat_mul_mfma_multi([up16(w) for w in ws], up16(a))
-    rng = np.random.default_rng(3)
     for i, (w, o) in enumerate(zip(ws, outs)):
-        rows = w.shape[0]
-        rr, cc = rng.integers(0, rows, 3000), rng.integers(0, n, 3000)
-        e, _ = mfma_error(orc, w, a, o.cpu().numpy(), rr, cc)
-        assert e <= MFMA_TOL, (i, e)
+        rr, cc = tile_samples(w.shape[0], n, 3 + i)
+        mfma_check(orc, w, a, o.cpu().numpy(), rr, cc, "grouped mfma matrix %d %s" % (i, shapes[i]))
 
 
 # ---------------------------------------------------------- edge cases
@@ -450,12 +492,14 @@ def test_large_magnitudes_and_cancellation(orc):
             assert_bits_equal(got.cpu().numpy(), orc.mat_mul(w, a[:nn]), "magnitudes k=%d n=%d" % (k, nn))
 
 
-def test_tinyblas_order_special_values(orc):
+@pytest.mark.parametrize("rows,k,n", [(136, 264, 133), (1064, 264, 1000)])
+def test_tinyblas_order_special_values(orc, rows, k, n):
     """The tinyBLAS order (computed one chain step per fp32 MFMA) on rows and
     columns made of signed zeros, subnormals, the f16 extremes, infinities
     and NaNs, over several output tiles with ragged edges; also an unaligned
-    activation pointer (the guarded-load kernel)."""
-    rows, k, n = 136, 264, 133
+    activation pointer (the guarded-load kernel).  136 x 133 (25 32 x 32
+    tiles) runs one tile per block; 1064 x 1000 (1088 tiles) runs the 64 x 64
+    blocks, with ragged last row and column blocks."""
     rng = np.random.default_rng(45)
     w = synth.random_f16(61, (rows, k), 0.02)
     a = synth.random_f16(62, (n, k))
@@ -466,17 +510,101 @@ def test_tinyblas_order_special_values(orc):
     w[70, 9] = 0x7C00                                   # +inf in the second row tile
     w[71, 17] = 0x7E00                                  # NaN
     w[72, 3], w[72, 11] = 0x7C00, 0xFC00                # inf and -inf in one row: NaN
-    w[135, 263] = 0xFC00                                # -inf in the last row, last step
+    w[rows - 1, k - 1] = 0xFC00                         # -inf in the last row, last step
     a[0, :] = 0x8000                                    # -0 column
     a[1, :] = rng.integers(1, 0x400, k)                 # subnormal column
     a[2, 5] = 0x7C00                                    # inf meets finite and zero weights
-    a[130, ::3] = 0x7BFF                                # a column in the ragged last tile
+    a[n - 3, ::3] = 0x7BFF                              # a column in the ragged last tile
     assert f16wm.takes_sgemm(rows, k, n)
-    want = orc.mat_mul(w, a)
+    want = orc.mat_mul(w, a, threads=HOST_T)
     got = f16wm.mat_mul(up16(w), up16(a))
     assert_bits_equal(got.cpu().numpy(), want, "tinyBLAS specials")
     got = f16wm.mat_mul(up16(w), up16(a, offset=1))
     assert_bits_equal(got.cpu().numpy(), want, "tinyBLAS specials, unaligned activation")
+
+
+def _f16(v) -> int:
+    """The f16 bit pattern of a value that f16 holds exactly."""
+    h = np.array([v], dtype=np.float16)
+    assert float(h[0]) == v or (np.isnan(v) and np.isnan(h[0]))
+    return int(h.view(np.uint16)[0])
+
+
+# One chain step of the tinyBLAS order is acc = fma(w, a, acc): with f16
+# operands the product is exact in binary32, so the step is the binary32 sum
+# acc + w*a rounded to nearest, ties to even.  The exact GEMM kernels compute
+# it as one rank-1 update of v_mfma_f32_32x32x1_2b_f32.  Each case below is
+# (chain lane, [(step, w, a), ...], expected element) for a k = 64 row and
+# column (eight steps per chain lane, every other element zero), so the
+# element's other seven lanes are +0 and the hsum adds only exact zeros.
+_STEP_CASES = [
+    # name, lane, steps, expected f32 value
+    ("tie to even (down)", 0, [(0, 1.0, 1.0), (1, 2.0 ** -12, 2.0 ** -12)], 1.0),
+    ("tie to even (up)", 3, [(0, 1.0, 1.0), (1, 2.0 ** -12, 2.0 ** -11), (2, 2.0 ** -12, 2.0 ** -12)],
+     1.0 + 2.0 ** -22),
+    ("above the tie", 5, [(0, 1.0, 1.0), (1, 2.0 ** -12 * (1 + 2.0 ** -6), 2.0 ** -12)], 1.0 + 2.0 ** -23),
+    ("below the tie", 7, [(0, 1.0, 1.0), (1, 2.0 ** -12 * (1 - 2.0 ** -11), 2.0 ** -12)], 1.0),
+    ("negative tie to even", 4, [(0, 1.0, 1.0), (3, -(2.0 ** -12), 2.0 ** -13)], 1.0),
+    ("exact cancellation gives +0", 1, [(0, 1.0, 1.0), (5, -1.0, 1.0)], 0.0),
+    ("cancellation at 2^32", 6, [(0, 65504.0, 65504.0), (1, -65504.0, 65504.0), (7, 1.0, 1.0)], 1.0),
+    ("absorbed below half an ulp", 2, [(0, 65504.0, 65504.0), (1, 2.0 ** -14, 2.0 ** -14)],
+     65504.0 * 65504.0),
+    ("+inf then finite", 0, [(0, np.inf, 1.0), (4, -3.0, 2.0)], np.inf),
+    ("+inf plus -inf", 5, [(2, np.inf, 1.0), (6, -np.inf, 1.0)], np.nan),
+    ("NaN operand", 3, [(1, np.nan, 1.0), (2, 1.0, 1.0)], np.nan),
+]
+
+
+def _step_case_operands(k=64):
+    rows = []
+    for name, lane, steps, want in _STEP_CASES:
+        wv = np.zeros(k, np.uint16)
+        av = np.zeros(k, np.uint16)
+        for t, x, y in steps:
+            wv[8 * t + lane] = _f16(x)
+            av[8 * t + lane] = _f16(y)
+        rows.append((name, wv, av, want))
+    # -0 products onto +0 accumulators in all eight lanes: every step adds
+    # -0 to +0, which is +0, so the element is +0 (a -0 in all eight lanes
+    # would survive the hsum)
+    rows.append(("-0 products onto +0", np.full(k, 0x8000, np.uint16), np.full(k, _f16(1.5), np.uint16), 0.0))
+    return rows
+
+
+@pytest.mark.parametrize("rows,n,f32act,aoff", [(64, 40, False, 0), (1064, 1000, False, 0),
+                                                (1064, 1000, True, 0), (1064, 1000, False, 1)])
+def test_fp32_mfma_chain_step_rounding(orc, rows, n, f32act, aoff):
+    """The rounding of one chain step on the fp32 matrix cores: ties to even
+    in both directions, just above and below a tie, a negative tie, exact
+    cancellation to +0, -0 products onto +0 accumulators, absorption at
+    2^32, infinities and NaN.  Each case sits at a (row, column) pair spread
+    over the output tiles (the first, the middle and the ragged last ones)
+    in a background of random values; its element must equal the value the
+    IEEE definition gives (worked out above, independent of the oracle) and
+    the whole product must equal the oracle bit for bit.  64 x 40 runs one
+    tile per block, 1064 x 1000 the 64 x 64 blocks (f16 or f32 activation
+    block, aligned or guarded loads)."""
+    k = 64
+    w = synth.random_f16((95, rows, k), (rows, k), 0.02)
+    a = synth.random_f16((96, n, k), (n, k))
+    cases = _step_case_operands(k)
+    pos_r = np.linspace(0, rows - 1, len(cases)).astype(np.int64)
+    pos_c = np.linspace(n - 1, 0, len(cases)).astype(np.int64)
+    for (name, wv, av, _), r, c in zip(cases, pos_r, pos_c):
+        w[r] = wv
+        a[c] = av
+    if f32act:
+        got = f16wm.mat_mul(up16(w), up32(orc.widen(a), aoff)).cpu().numpy()
+    else:
+        got = f16wm.mat_mul(up16(w), up16(a, aoff)).cpu().numpy()
+    for (name, _, _, want), r, c in zip(cases, pos_r, pos_c):
+        g = got[c, r]
+        if np.isnan(want):
+            assert np.isnan(g), (name, g)
+        else:
+            assert np.float32(g).view(np.uint32) == np.float32(want).view(np.uint32), \
+                "%s at (%d, %d): got %r, IEEE gives %r" % (name, r, c, float(g), want)
+    assert_bits_equal(got, orc.mat_mul(w, a, threads=HOST_T), "chain-step cases %dx%d n=%d" % (rows, k, n))
 
 
 def test_repeatable_bits():
@@ -518,39 +646,72 @@ def test_binding_reports_library_errors():
 
 # ------------------------------------------------------------ MFMA path
 
-def mfma_error(orc, w, a, got, rr, cc):
+def tile_samples(rows, n, seed, per=16, blk=64):
+    """`per` seeded random elements in every blk x blk block of a rows x n
+    output, ragged edge blocks included (every tile shape the MFMA kernels
+    use, 256 x 256 down to 128 x 64, is a union of 64 x 64 blocks).
+    Returns (row indices, column indices)."""
+    rng = np.random.default_rng(seed)
+    r0, c0 = np.meshgrid(np.arange(0, rows, blk), np.arange(0, n, blk), indexing="ij")
+    r0, c0 = r0.ravel(), c0.ravel()
+    hr, hc = np.minimum(blk, rows - r0), np.minimum(blk, n - c0)
+    rr = r0[:, None] + (rng.random((r0.size, per)) * hr[:, None]).astype(np.int64)
+    cc = c0[:, None] + (rng.random((c0.size, per)) * hc[:, None]).astype(np.int64)
+    return rr.ravel(), cc.ravel()
+
+
+def f32_accumulation_bound(k: int) -> float:
+    """Relative bound (times sum |w a|) on an fp16 MFMA product with f32
+    accumulation over k, and on the binary64 reference's own error.  Every
+    f16 x f16 product is exact; one v_mfma_f32_32x32x16_f16 adds 16 of them to
+    the f32 accumulator, so with any internal order of at least f32 precision
+    each product passes through at most ceil(k/16) + 15 roundings of unit
+    2^-24: recursive summation gives |y - exact| <= gamma_m * sum|w a| with
+    m = ceil(k/16) + 16 (one spare) and gamma_m = m u / (1 - m u).  The
+    binary64 reference adds at most k * 2^-53 * sum|w a|."""
+    m = -(-k // 16) + 16
+    u = 2.0 ** -24
+    return m * u / (1 - m * u) + k * 2.0 ** -53
+
+
+def mfma_check(orc, w, a, got, rr, cc, what):
+    """The MFMA product at the sampled elements against the binary64
+    reference: (1) the gate max |y - ref| / sum|w a| <= 2e-3; (2) the f32
+    accumulation bound above, element by element; (3) the plain relative
+    error |y - ref| / |ref| <= 2e-3 on elements with |ref| >= 1e-2 rms(ref).
+    Returns (max gate ratio, max relative error)."""
     ref, scale = orc.fp64_at(w, a, rr, cc)
     y = got[cc, rr].astype(np.float64)
-    err = np.abs(y - ref) / np.maximum(scale, 1e-300)
+    d = np.abs(y - ref)
+    err = d / np.maximum(scale, 1e-300)
+    gate = float(err.max())
+    assert gate <= MFMA_TOL, "%s: max |y-ref|/sum|wa| = %.3g" % (what, gate)
+    bound = f32_accumulation_bound(w.shape[1]) * scale
+    bad = d > bound
+    if bad.any():
+        i = int(np.argmax(bad))
+        raise AssertionError("%s: %d of %d sampled elements exceed the f32 accumulation bound; first (r=%d, c=%d): "
+                             "|y-ref| = %.3g > %.3g" % (what, int(bad.sum()), d.size, rr[i], cc[i], d[i], bound[i]))
     rms = np.sqrt(np.mean(ref ** 2))
     big = np.abs(ref) >= 1e-2 * rms
-    rel = np.abs(y - ref)[big] / np.abs(ref)[big]
-    return float(err.max()), float(rel.max()) if big.any() else 0.0
+    rel = float((d[big] / np.abs(ref[big])).max()) if big.any() else 0.0
+    assert rel <= MFMA_TOL, "%s: max relative error %.3g on |ref| >= 1e-2 rms" % (what, rel)
+    return gate, rel
 
 
 @pytest.mark.parametrize("rows,k,n", [(128, 32, 128), (200, 40, 130), (576, 576, 512), (1, 8, 1),
-                                      (1000, 4104, 77), (49152, 576, 16)])
+                                      (1000, 4104, 77), (49152, 576, 16), (4100, 1000, 300)])
 def test_mfma_small_shapes(orc, rows, k, n):
     w = synth.random_f16((61, rows, k), (rows, k), 0.02)
     a = synth.random_f16((62, rows, k), (n, k))
     got = f16wm.mat_mul_mfma(up16(w), up16(a)).cpu().numpy()
-    rng = np.random.default_rng(1)
-    m = min(rows * n, 20000)
-    rr = rng.integers(0, rows, m)
-    cc = rng.integers(0, n, m)
-    e, rel = mfma_error(orc, w, a, got, rr, cc)
-    say("mfma %dx%d n=%d: max err/sum|wa| = %.3g, max rel = %.3g" % (rows, k, n, e, rel))
-    assert e <= MFMA_TOL
+    rr, cc = tile_samples(rows, n, 1)
+    e, rel = mfma_check(orc, w, a, got, rr, cc, "mfma %dx%d n=%d" % (rows, k, n))
+    say("mfma %dx%d n=%d: %d samples, max err/sum|wa| = %.3g (bound %.3g), max rel = %.3g"
+        % (rows, k, n, rr.size, e, f32_accumulation_bound(k), rel))
 
 
 # ----------------------------------------------- full-size model shapes
-
-def _sample(rows, n, m, seed):
-    rng = np.random.default_rng(seed)
-    rr = np.concatenate([rng.integers(0, rows, m), [0, rows - 1, 0, rows - 1]])
-    cc = np.concatenate([rng.integers(0, n, m), [0, 0, n - 1, n - 1]])
-    return rr, cc
-
 
 def test_smollm2_135m_decode_step_all_matrices(orc):
     """Every product of a 135M-shaped decode step (30 distinct layers + the tied
@@ -581,25 +742,22 @@ def test_smollm2_135m_decode_step_all_matrices(orc):
 
 
 def test_smollm2_135m_prefill_512(orc):
-    """n = 512 micro-batch on the 135M matrices (tinyBLAS order): layer 0 in
-    full, the logits on sampled elements; MFMA within tolerance."""
-    S = synth.SMOLLM2_135M
+    """n = 512 micro-batch on the 135M matrices (tinyBLAS order): layer 0 and
+    the tied 49152x576 logits, every element bit-exact; the MFMA product
+    sampled in every 64 x 64 output block."""
+    S = dict(synth.SMOLLM2_135M)
+    S["logits"] = synth.SMOLLM2_135M_LOGITS
     acts = synth.activation(synth.CFG_135M_PREFILL, 0, 0, synth.PREFILL_N, 1536)
-    for m, (rows, k) in S.items():
+    for i, (m, (rows, k)) in enumerate(S.items()):
         w = synth.weight(synth.CFG_135M, 0, m, rows, k)
         a16 = orc.to_f16(acts[:, :k])
         got = f16wm.mat_mul(up16(w), up16(a16)).cpu().numpy()
-        assert_bits_equal(got, orc.mat_mul(w, a16), "135M prefill layer 0 %s" % m)
+        assert_bits_equal(got, orc.mat_mul(w, a16, threads=HOST_T), "135M prefill layer 0 %s" % m)
         gm = f16wm.mat_mul_mfma(up16(w), up16(a16)).cpu().numpy()
-        rr, cc = _sample(rows, synth.PREFILL_N, 4000, 3)
-        e, _ = mfma_error(orc, w, a16, gm, rr, cc)
-        say("135M prefill %s exact ok; mfma err %.3g" % (m, e))
-        assert e <= MFMA_TOL
-    wl = synth.weight(synth.CFG_135M, 0, "logits", *synth.SMOLLM2_135M_LOGITS)
-    a16 = orc.to_f16(acts[:, :576])
-    got = f16wm.mat_mul(up16(wl), up16(a16)).cpu().numpy()
-    rr, cc = _sample(wl.shape[0], synth.PREFILL_N, 20000, 4)
-    assert_bits_equal(got[cc, rr], orc.mat_mul_at(wl, a16, rr, cc), "135M prefill logits (sampled)")
+        rr, cc = tile_samples(rows, synth.PREFILL_N, 30 + i)
+        e, rel = mfma_check(orc, w, a16, gm, rr, cc, "135M prefill mfma %s" % m)
+        say("135M prefill %s: exact ok (%d elements); mfma err %.3g rel %.3g over %d samples"
+            % (m, got.size, e, rel, rr.size))
 
 
 def test_llama3_8b_decode_gemv_all_matrices(orc):
@@ -624,24 +782,222 @@ def test_llama3_8b_decode_gemv_all_matrices(orc):
         say("8B gemv %s ok" % m)
 
 
-def test_llama3_8b_prefill_512(orc):
-    """n = 512 on the 8B matrices: exact order on sampled elements (the oracle
-    would need minutes for all 3.8e11 FMAs), MFMA within tolerance."""
-    S = dict(synth.LLAMA3_8B)
-    S["logits"] = synth.LLAMA3_8B_LOGITS
+_8B_ALL = dict(synth.LLAMA3_8B, logits=synth.LLAMA3_8B_LOGITS)
+
+
+@pytest.mark.parametrize("m", list(_8B_ALL))
+def test_llama3_8b_prefill_512(orc, m):
+    """n = 512 on each 8B matrix: the exact order on EVERY element against the
+    oracle (all 7.6e11 flops of the set, the oracle on the host's cores), and
+    the MFMA product sampled in every 64 x 64 output block."""
+    rows, k = _8B_ALL[m]
+    i = list(_8B_ALL).index(m)
     acts = synth.activation(synth.CFG_8B_PREFILL, 0, 0, synth.PREFILL_N, 14336)
-    for i, (m, (rows, k)) in enumerate(S.items()):
+    w = synth.weight(synth.CFG_8B, 0, m, rows, k)
+    a16 = orc.to_f16(acts[:, :k])
+    del acts
+    wd, ad = up16(w), up16(a16)
+    got = f16wm.mat_mul(wd, ad).cpu().numpy()
+    gm = f16wm.mat_mul_mfma(wd, ad).cpu().numpy()
+    del wd, ad
+    say("8B prefill %s: %dx%d n=512 on the GPU; oracle on %d threads" % (m, rows, k, HOST_T))
+    assert_bits_equal(got, orc.mat_mul(w, a16, threads=HOST_T), "8B prefill %s" % m)
+    rr, cc = tile_samples(rows, synth.PREFILL_N, 10 + i)
+    e, rel = mfma_check(orc, w, a16, gm, rr, cc, "8B prefill mfma %s" % m)
+    say("8B prefill %s: exact ok (%d elements); mfma err %.3g (bound %.3g) rel %.3g over %d samples"
+        % (m, got.size, e, f32_accumulation_bound(k), rel, rr.size))
+
+
+# ------------------------------------------- decode sequences as HIP graphs
+
+def _replay_and_check(graph, outs, wants, what, eager=None, replays=3):
+    """Replays `graph` several times, with the outputs poisoned before each
+    replay and eager library work (and a synchronisation) between replays;
+    every output of every replay must equal the oracle bit for bit."""
+    for rep in range(replays):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (o, wnt) in enumerate(zip(outs, wants)):
+            assert_bits_equal(o.cpu().numpy(), wnt, "%s replay %d output %d" % (what, rep, i))
+        if eager is not None:
+            eager()
+            torch.cuda.synchronize()
+    say("%s: %d replays bit-exact (%d outputs each)" % (what, replays, len(outs)))
+
+
+def test_smollm2_135m_decode_step_as_graph(orc):
+    """The 135M-shaped decode step as the benchmark runs it: 30 layers x
+    {Q/K/V grouped, O, gate/up grouped, down} + the tied 49152x576 logits,
+    121 launches taking f32 columns (rounded inside each launch), captured
+    once as a HIP graph and replayed; every one of the 211 outputs against
+    the oracle on every replay."""
+    S = synth.SMOLLM2_135M
+    L = synth.SMOLLM2_135M_LAYERS
+    groups = [("qkv", ["q", "k", "v"], 576), ("o", ["o"], 576), ("gateup", ["gate", "up"], 576),
+              ("down", ["down"], 1536)]
+    W, X, O, want = {}, {}, {}, {}
+    for l in range(L):
+        acts = synth.activation(synth.CFG_135M, l, 0, 4, 1536)
+        for gi, (g, mats, k) in enumerate(groups):
+            x = np.ascontiguousarray(acts[gi, :k])
+            X[(l, g)] = up32(x)
+            x16 = orc.to_f16(x)
+            for m in mats:
+                w = synth.weight(synth.CFG_135M, l, m, *S[m])
+                W[(l, m)] = up16(w)
+                O[(l, m)] = torch.empty(S[m][0], dtype=torch.float32, device=DEV)
+                want[(l, m)] = orc.mat_vec(w, x16, threads=HOST_T)
+    wl = synth.weight(synth.CFG_135M, 0, "logits", *synth.SMOLLM2_135M_LOGITS)
+    xl = np.ascontiguousarray(synth.activation(synth.CFG_135M, L, 0, 1, 576)[0])
+    W["logits"], X["logits"] = up16(wl), up32(xl)
+    O["logits"] = torch.empty(wl.shape[0], dtype=torch.float32, device=DEV)
+    want["logits"] = orc.mat_vec(wl, orc.to_f16(xl), threads=HOST_T)
+
+    def step():
+        for l in range(L):
+            for g, mats, _ in groups:
+                if len(mats) > 1:
+                    f16wm.mat_vec_multi([W[(l, m)] for m in mats], X[(l, g)], [O[(l, m)] for m in mats])
+                else:
+                    f16wm.mat_vec(W[(l, mats[0])], X[(l, g)], O[(l, mats[0])])
+        f16wm.mat_vec(W["logits"], X["logits"], O["logits"])
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    keys = list(want)
+    _replay_and_check(graph, [O[key] for key in keys], [want[key] for key in keys], "135M decode step graph",
+                      eager=step)
+    del graph
+
+    # the same 211 products as one table (f16wm_mat_vec_table): eagerly, then
+    # captured and replayed
+    src = {"q": "qkv", "k": "qkv", "v": "qkv", "o": "o", "gate": "gateup", "up": "gateup", "down": "down"}
+    T = {key: torch.empty_like(o) for key, o in O.items()}
+    table = f16wm.VecTable([(W[(l, m)], X[(l, src[m])], T[(l, m)]) for l in range(L) for m in S] +
+                           [(W["logits"], X["logits"], T["logits"])])
+    for o in T.values():
+        o.fill_(float("nan"))
+    table()
+    torch.cuda.synchronize()
+    for key in keys:
+        assert_bits_equal(T[key].cpu().numpy(), want[key], "135M decode table %s" % (key,))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        table()
+    torch.cuda.synchronize()
+    _replay_and_check(graph, [T[key] for key in keys], [want[key] for key in keys], "135M decode step table graph",
+                      eager=step)
+    del graph
+
+
+def test_llama3_8b_decode_set_as_graph(orc):
+    """The 8B-shaped decode set as the benchmark runs it (Q/K/V grouped, O,
+    gate/up grouped, down, logits; f32 columns rounded inside each launch),
+    captured once as a HIP graph and replayed; all eight outputs against the
+    oracle on every replay."""
+    S = dict(synth.LLAMA3_8B, logits=synth.LLAMA3_8B_LOGITS)
+    acts = synth.activation(synth.CFG_8B, 0, 0, 5, 14336)
+    dec_k = {"attn": 4096, "o": 4096, "ffn": 4096, "down": 14336, "logits": 4096}
+    X = {g: up32(np.ascontiguousarray(acts[i, :dec_k[g]])) for i, g in enumerate(dec_k)}
+    x16 = {g: orc.to_f16(acts[i, :dec_k[g]]) for i, g in enumerate(dec_k)}
+    src = {"q": "attn", "k": "attn", "v": "attn", "o": "o", "gate": "ffn", "up": "ffn", "down": "down",
+           "logits": "logits"}
+    W, O, want = {}, {}, {}
+    for m, (rows, k) in S.items():
         w = synth.weight(synth.CFG_8B, 0, m, rows, k)
-        a16 = orc.to_f16(acts[:, :k])
-        wd, ad = up16(w), up16(a16)
-        got = f16wm.mat_mul(wd, ad).cpu().numpy()
-        rr, cc = _sample(rows, synth.PREFILL_N, 3000, 10 + i)
-        assert_bits_equal(got[cc, rr], orc.mat_mul_at(w, a16, rr, cc), "8B prefill %s (sampled)" % m)
-        gm = f16wm.mat_mul_mfma(wd, ad).cpu().numpy()
-        e, rel = mfma_error(orc, w, a16, gm, rr, cc)
-        say("8B prefill %s: exact ok; mfma err %.3g rel %.3g" % (m, e, rel))
-        assert e <= MFMA_TOL
-        del wd, ad
+        W[m] = up16(w)
+        O[m] = torch.empty(rows, dtype=torch.float32, device=DEV)
+        want[m] = orc.mat_vec(w, x16[src[m]], threads=HOST_T)
+        del w
+
+    def step():
+        f16wm.mat_vec_multi([W["q"], W["k"], W["v"]], X["attn"], [O["q"], O["k"], O["v"]])
+        f16wm.mat_vec(W["o"], X["o"], O["o"])
+        f16wm.mat_vec_multi([W["gate"], W["up"]], X["ffn"], [O["gate"], O["up"]])
+        f16wm.mat_vec(W["down"], X["down"], O["down"])
+        f16wm.mat_vec(W["logits"], X["logits"], O["logits"])
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    _replay_and_check(graph, [O[m] for m in S], [want[m] for m in S], "8B decode set graph", eager=step)
+    del graph
+
+    # the eight products as one table launch, eagerly and as a graph
+    T = {m: torch.empty_like(O[m]) for m in S}
+    table = f16wm.VecTable([(W[m], X[src[m]], T[m]) for m in S])
+    for o in T.values():
+        o.fill_(float("nan"))
+    table()
+    torch.cuda.synchronize()
+    for m in S:
+        assert_bits_equal(T[m].cpu().numpy(), want[m], "8B decode table %s" % m)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        table()
+    torch.cuda.synchronize()
+    _replay_and_check(graph, [T[m] for m in S], [want[m] for m in S], "8B decode set table graph", eager=step)
+    del graph
+
+
+def _table_case(orc, seed, rows, k, f32, off=0):
+    """A product's weight and column (host and device; f32 columns also
+    rounded by the oracle)."""
+    w = synth.random_f16((seed, rows, k, 1), (rows, k), 0.02)
+    if f32:
+        x = f32_column((seed, rows, k, 2), k)
+        return w, x, orc.to_f16(x), up16(w), up32(x, off)
+    a = synth.random_f16((seed, rows, k, 2), (k,))
+    return w, a, a, up16(w), up16(a, off)
+
+
+def test_mat_vec_table_every_kernel_class(orc):
+    """One f16wm_mat_vec_table call over 230 products of every kind: short
+    rows (k <= 640, registers) and staged rows (k up to 16384 with the whole
+    column in LDS, and k = 16392 without), f16 and f32 columns (the rounding's
+    edge values included), k % 32 tails, rows that leave a ragged last tile,
+    empty matrices, k = 0, a shared column and a shared weight, more than 96
+    products of one class (several launches), and misaligned or k % 8 != 0
+    products that fall back to their own launches.  Every element against the
+    oracle."""
+    rng = np.random.default_rng(97)
+    shapes = []
+    for i in range(110):                     # > 96 products of the short-row f16 class
+        shapes.append((int(rng.integers(1, 70)), int(rng.choice([8, 32, 40, 576, 640])), False, 0))
+    for i in range(40):                      # short rows, f32 columns
+        shapes.append((int(rng.integers(1, 300)), int(rng.choice([64, 200, 576])), True, 0))
+    for i in range(40):                      # staged rows
+        shapes.append((int(rng.integers(1, 400)), int(rng.choice([648, 1000, 1536, 4096, 4104])), bool(i % 2), 0))
+    shapes += [(4096, 14336, False, 0), (1000, 14336, True, 0), (33, 16384, False, 0), (17, 16392, True, 0),
+               (70, 16392, False, 0), (0, 576, False, 0), (5, 0, False, 0), (16, 33, False, 0), (9, 100, True, 1),
+               (40, 1000, False, 1), (3, 31, True, 0)]
+    prods, wants = [], []
+    for i, (rows, k, f32, off) in enumerate(shapes):
+        w, x, x16, wd, xd = _table_case(orc, 2000 + i, rows, k, f32, off)
+        prods.append((wd, xd))
+        wants.append(orc.mat_vec(w, x16, threads=HOST_T) if rows else np.zeros(0, np.float32))
+    # a shared column (product 0's) and a shared weight (product 1's)
+    w0, _, x16_0, _, _ = _table_case(orc, 2000, *shapes[0][:3])
+    prods.append((up16(w0), prods[0][1]))
+    wants.append(orc.mat_vec(w0, x16_0, threads=HOST_T))
+    w1, _, _, _, _ = _table_case(orc, 2001, *shapes[1][:3])
+    a_new = synth.random_f16(3000, (shapes[1][1],))
+    prods.append((prods[1][0], up16(a_new)))
+    wants.append(orc.mat_vec(w1, a_new, threads=HOST_T))
+    say("mat_vec_table: %d products" % len(prods))
+    outs = f16wm.mat_vec_table(prods)
+    for i, (o, wnt) in enumerate(zip(outs, wants)):
+        assert_bits_equal(o.cpu().numpy(), wnt, "table product %d %s" % (i, shapes[i] if i < len(shapes) else "shared"))
 
 
 # ------------------------------------------------------------- next rows

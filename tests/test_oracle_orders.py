@@ -9,8 +9,9 @@ The bankML f16 page (Design notes) defines:
 The page prints no worked example, so each pin below is derived: exact integer
 sums, one-hot rows, hand-built inputs whose value under each tree is worked out
 by hand (cases A-E), invariance groups of each tree, textbook summation for
-k < 32, an error bound against an exact fixed-point sum, and the page's own
-claim that the two orders give different bits on the same inputs.  A dropped
+k < 32, an error bound against an exact fixed-point sum, and the point the
+page makes in its Summary, that one row and column reduced in the two orders
+need not agree bit for bit.  A dropped
 or repeated term, a wrong sign or index, a transposed operand, a wrong tree
 level or a tail summed in f32 each fails at least one of them.
 """
@@ -291,9 +292,11 @@ def test_takes_sgemm_truth_table(orc):
 
 
 def test_the_two_reductions_differ(orc):
-    """The page's claim: the two paths give different bits for the same row and
-    column, so the path choice has to be checked too.  576x576 weight, 3
-    columns of f16-rounded N(0,1) activations."""
+    """f16 page, Summary: the vec_dot and tinyBLAS reductions of one row and
+    one column are not bit-interchangeable, which is why the shape rule that
+    picks between them needs its own check.  Here most elements of the 576x576
+    weight times 3 f16-rounded N(0,1) columns come out differently in the two
+    orders, while staying within rounding distance of each other."""
     w, a = synth.c1()
     a16 = orc.to_f16(a)
     vd = np.array([[orc.vec_dot(w[r], a16[c]) for r in range(576)] for c in range(3)])
