@@ -3,10 +3,12 @@
 
 One step is one pass of the whole hot path over one batch of synthetic input:
 
-  decode (n = 1):  Q/K/V grouped GEMV, O GEMV, gate/up grouped GEMV, down
-                   GEMV and the 128256x4096 logits GEMV (vec_dot order), each
-                   taking its f32 activation column and rounding it to f16
-                   (to_f16, same code) inside the same launch;
+  decode (n = 1):  the eight GEMVs of the set (q, k, v, o, gate, up, down and
+                   the 128256x4096 logits, vec_dot order), each taking its own
+                   f32 activation column and rounding it to f16 (to_f16, same
+                   code) inside the launch, as ONE f16wm_mat_vec_table launch
+                   (the products are independent: every column is a seeded
+                   input);
   prefill (n = 512): to_f16 of each 512-column activation block, then the
                    exact product of every matrix (tinyBLAS order, picked by
                    takes_sgemm) and the MFMA fp16 product of every matrix.
@@ -16,10 +18,12 @@ activations) resident in HBM before the timed region.  The weight set is
 1.49 GB, well above the 256 MB last-level cache, so each step streams it cold.
 
 Prints ONE JSON line.  `value` is the decode GEMV throughput in GB/s:
-algorithmic bytes of the decode step / its time (HIP events around the five
-launches of each timed step, nothing recorded between them).  The same five
-launches captured as a HIP graph are timed beside it (bit-identical), and
-the n = 512 GEMM throughputs are reported under "gemm_n512"."""
+algorithmic bytes of the set / the table launch's time (HIP events around it
+in each timed step).  Beside it: the same products as the five dependent
+launches a model's layer issues (eager and as a HIP graph), per-launch
+distributions (median, p10, p90 over --dist launches), the n = 512 GEMM
+throughputs ("gemm_n512", with the logits launch of each on its own), the
+576x576 case, the 135M-shaped step, and the oracle timed on the host."""
 from __future__ import annotations
 
 import argparse
@@ -49,6 +53,8 @@ def parse():
                    help="the oracle's prefill sample is rows/N of every matrix")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    p.add_argument("--dist", type=int, default=50,
+                   help="launches per timing distribution (median, p10, p90)")
     return p.parse_args()
 
 
@@ -148,8 +154,16 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    def decode():
-        # decode, n = 1 (f32 columns, rounded to f16 inside each product)
+    # The decode GEMV set as one table launch: the eight products, each with
+    # its own f32 column (rounded inside the launch), are independent here
+    # (every column is a seeded input), so f16wm_mat_vec_table runs them in
+    # one launch.  In a forward pass the same call takes the products of one
+    # dependency level.
+    table = f16wm.VecTable([(W[m], X1[src_of[m]], O1[m]) for m in S])
+
+    def decode_sequence():
+        # the same products as a model's layer issues them: Q/K/V grouped, O,
+        # gate/up grouped, down, logits (five launches)
         for name, mats, g in gemv_launches:
             if len(mats) > 1:
                 f16wm.mat_vec_multi([W[m] for m in mats], X1[g], [O1[m] for m in mats])
@@ -160,7 +174,7 @@ def main():
         e = [ev() for _ in range(4)] if timed else None
         if timed:
             e[0].record()
-        decode()
+        table()
         if timed:
             e[1].record()
         # ---- prefill, n = 512, exact order (takes_sgemm holds for every shape);
@@ -197,18 +211,24 @@ def main():
     wall_s = time.perf_counter() - t_start
 
     K = args.steps
-    dec_eager_avg = sum(e[0].elapsed_time(e[1]) for e in recs) / K
+    dec_table_avg = sum(e[0].elapsed_time(e[1]) for e in recs) / K
     exact_avg = sum(e[1].elapsed_time(e[2]) for e in recs) / K
     mfma_avg = sum(e[2].elapsed_time(e[3]) for e in recs) / K
+    value = decode_bytes / (dec_table_avg * 1e-3) / 1e9
+    want = {m: O1[m].view(torch.int32).clone() for m in S}
 
-    # The decode step's five launches captured once as a HIP graph and
-    # replayed (one replay streams the whole 1.49 GB weight set, six times the
-    # last-level cache, so every replay reads cold); replays are checked bit
-    # for bit against the eager step.
-    want = [O1[m].view(torch.int32).clone() for m in S]
+    # Distribution of the table launch: NDIST launches, each between its own
+    # pair of events (event overhead included; the roofline below uses
+    # back-to-back launches instead).
+    table_ms = per_launch_ms(torch, ev, table, args.dist)
+
+    # The dependent five-launch sequence, eager and as a HIP graph (the
+    # weight set is six times the last-level cache: every pass is cold).
+    seq_ms = per_launch_ms(torch, ev, decode_sequence, args.dist)
+    seq_same = all(torch.equal(O1[m].view(torch.int32), want[m]) for m in S)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        decode()
+        decode_sequence()
     torch.cuda.synchronize()
     graph_same = True
     for _ in range(2):
@@ -216,20 +236,12 @@ def main():
             O1[m].fill_(float("nan"))
         graph.replay()
         torch.cuda.synchronize()
-        graph_same = graph_same and all(torch.equal(O1[m].view(torch.int32), w) for m, w in zip(S, want))
-    gre = [(ev(), ev()) for _ in range(K)]
-    for a, b in gre:
-        a.record()
-        graph.replay()
-        b.record()
-    torch.cuda.synchronize()
-    dec_graph_avg = sum(a.elapsed_time(b) for a, b in gre) / K
+        graph_same = graph_same and all(torch.equal(O1[m].view(torch.int32), want[m]) for m in S)
+    seq_graph_ms = per_launch_ms(torch, ev, graph.replay, args.dist)
     del graph
-    dec_avg = dec_eager_avg
-    value = decode_bytes / (dec_avg * 1e-3) / 1e9
 
-    # Per-launch decode timings: the same launches again, each between two
-    # HIP events on the stream the library launches on (torch's current).
+    # Per-launch timings of the sequence's five launches (events between
+    # launches: dispatch and event overhead included).
     gemv_ms = []
     for _ in range(K):
         ge = [(ev(), ev()) for _ in gemv_launches]
@@ -243,43 +255,36 @@ def main():
         gemv_ms.append(ge)
     torch.cuda.synchronize()
     gemv_ms = [[a.elapsed_time(b) for a, b in ge] for ge in gemv_ms]
-
-    # Roofline of the kernel `value` is about: vec_dot_lds<16>, the logits GEMV
-    # (70 % of the decode bytes); average duration of its launches: K of them
-    # back to back between two HIP events on the stream the library launches
-    # on (torch's current), so the events' own cost is spread over K launches.
-    # Each launch streams the 1.05 GB matrix, four times the last-level cache,
-    # so none of them finds its weights cached.
-    li = [name for name, _, _ in gemv_launches].index("logits")
-    ev0, ev1 = ev(), ev()
-    ev0.record()
-    for _ in range(K):
-        f16wm.mat_vec(W["logits"], X1["logits"], O1["logits"])
-    ev1.record()
-    torch.cuda.synchronize()
-    logits_ms = ev0.elapsed_time(ev1) / K
-    achieved = gemv_b[li] / (logits_ms * 1e-3) / 1e9
     per_launch = {name: {"bytes": gemv_b[i], "avg_us": round(1e3 * sum(r[i] for r in gemv_ms) / K, 2),
                          "GB_s": round(gemv_b[i] / (sum(r[i] for r in gemv_ms) / K * 1e-3) / 1e9, 1)}
                   for i, (name, _, _) in enumerate(gemv_launches)}
-    gemv_all_ms = sum(sum(r) for r in gemv_ms) / K
 
+    # Roofline of the kernel `value` measures: the table launch
+    # (vec_dot_lds_table: every product of the set is k >= 4096, so one LDS
+    # launch), K launches back to back between two HIP events on the stream
+    # the library launches on (torch's current stream).
+    tbl_ms = back_to_back_ms(torch, ev, table, max(K, 20))
+    achieved = decode_bytes / (tbl_ms * 1e-3) / 1e9
+    table_kernel = "vec_dot_lds_table<16, true, true>"
     rec = traffic_record(os.path.join(ROOT, "f16_weight_matrix_amd", "csrc", "vec_dot.hip"))
-    traffic = rec.get("bytes_per_launch") if rec and rec.get("kernel") == "vec_dot_lds<16, true, true>" else None
+    traffic = rec.get("bytes_per_launch") if rec and rec.get("kernel") == table_kernel else None
+
+    # The step's time-dominant kernel: the exact (tinyBLAS order) logits
+    # product at n = 512, and the MFMA logits product, each timed alone.
+    lo_flops = 2 * S["logits"][0] * S["logits"][1] * N
+    exact_lo_ms = back_to_back_ms(torch, ev, lambda: f16wm.mat_mul(W["logits"], AN["logits"], ON["logits"]),
+                                  max(4, K // 2))
+    mfma_lo_ms = back_to_back_ms(torch, ev, lambda: f16wm.mat_mul_mfma(W["logits"], AN["logits"], OM["logits"]),
+                                 max(K, 20))
+
+    # C1: the 576x576 weight at n = 1 and n = 3 (launch-bound; parity case).
+    c1 = c1_leg(f16wm, torch, np, synth, dev, ev, args.dist)
 
     # Next row beside the step: the embedding lookup of a 512-token micro-batch
     # from the tied 128256x4096 table (get_rows), timed on its own.
     ids = torch.from_numpy(np.random.default_rng(7).integers(0, S["logits"][0], N)).to(dev)
     emb = torch.empty((N, S["logits"][1]), dtype=torch.float32, device=dev)
-    for _ in range(3):
-        f16wm.get_rows(W["logits"], ids, emb)
-    ev0, ev1 = ev(), ev()
-    ev0.record()
-    for _ in range(20):
-        f16wm.get_rows(W["logits"], ids, emb)
-    ev1.record()
-    torch.cuda.synchronize()
-    gr_us = ev0.elapsed_time(ev1) * 1e3 / 20
+    gr_ms = back_to_back_ms(torch, ev, lambda: f16wm.get_rows(W["logits"], ids, emb), 20)
     gr_bytes = N * S["logits"][1] * (2 + 4) + N * 8
     attn = attention_helpers_leg(f16wm, torch, np, synth, dev, ev)
 
@@ -288,6 +293,8 @@ def main():
 
     exact_tflops = flops_n512 / (exact_avg * 1e-3) / 1e12
     mfma_tflops = flops_n512 / (mfma_avg * 1e-3) / 1e12
+    ex_lo_tf = lo_flops / (exact_lo_ms * 1e-3) / 1e12
+    mf_lo_tf = lo_flops / (mfma_lo_ms * 1e-3) / 1e12
 
     out = {
         "metric": "F16 GEMV GB/s (n=1) and GEMM TFLOP/s (n=512), % of MI355X roofline",
@@ -304,49 +311,117 @@ def main():
         "data": "synthetic: seeded N(0,0.02) f16 weights, N(0,1) f32 activations",
         "config": {
             "workload": "Llama-3-8B-shaped F16 set (q/o 4096x4096, k/v 1024x4096, gate/up 14336x4096, "
-                        "down 4096x14336, logits 128256x4096): decode GEMV n=1 + prefill n=512 exact and MFMA",
+                        "down 4096x14336, logits 128256x4096): the decode GEMV set at n=1 as one table launch of "
+                        "its eight independent products (value), then prefill n=512 exact and MFMA",
             "arithmetic": "f16 weights and rounded f16 activations widened exactly, f32 FMA chains in the exact "
                           "ggml orders; the MFMA fast path multiplies fp16 into f32",
             "decode_bytes_per_step": decode_bytes,
             "prefill_flops_per_product_set": flops_n512,
             "parallelism": "single GPU",
         },
-        "phases_ms": {"decode": round(dec_avg, 4),
-                      "decode_as_graph": round(dec_graph_avg, 4), "decode_graph_bits_equal_eager": graph_same,
+        "phases_ms": {"decode_table": round(dec_table_avg, 4),
                       "prefill_exact": round(exact_avg, 4), "prefill_mfma": round(mfma_avg, 4)},
+        "decode_table_launch_ms": stats(table_ms),
+        "decode_sequence": {
+            "what": "the same eight products as five dependent launches (Q/K/V grouped, O, gate/up grouped, down, "
+                    "logits), as a model's layer issues them",
+            "eager_ms": stats(seq_ms), "graph_ms": stats(seq_graph_ms),
+            "GB_s_eager_median": round(decode_bytes / (stats(seq_ms)["median"] * 1e-3) / 1e9, 1),
+            "GB_s_graph_median": round(decode_bytes / (stats(seq_graph_ms)["median"] * 1e-3) / 1e9, 1),
+            "bits_equal_table": seq_same, "graph_bits_equal_table": graph_same,
+            "per_launch": per_launch,
+            "per_launch_note": "each launch between its own pair of HIP events: dispatch and event overhead "
+                               "included (kernel durations: rocprofv3 kernel trace)"},
         "roofline": {
-            "kernel": "vec_dot_lds<16, true, true> (logits GEMV 128256x4096, f32 column rounded in staging, vec_dot order)",
+            "kernel": table_kernel + " (the whole 8B GEMV set in one launch, f32 columns rounded in staging, "
+                      "vec_dot order)",
+            "covers": "the kernel value measures; the step's time-dominant kernel is the exact logits GEMM, "
+                      "whose roofline is gemm_n512.exact.logits_launch",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "avg_launch_us": round(logits_ms * 1e3, 2),
-            "algorithmic_bytes_per_launch": gemv_b[li],
-            "all_gemv_launches_GB_s": round(sum(gemv_b) / (gemv_all_ms * 1e-3) / 1e9, 1),
-            "per_launch": per_launch,
-            "per_launch_note": "each launch between its own pair of HIP events: dispatch and event overhead "
-                               "included (kernel durations: rocprofv3 kernel trace)",
+            "avg_launch_us": round(tbl_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": decode_bytes,
         },
         "gemm_n512": {
             "exact": {"kernel": "tinyblas_mfma (tinyBLAS order, one chain step per fp32 MFMA 32x32x1)",
                       "bound": "mfma", "achieved": round(exact_tflops, 2), "unit": "TFLOP/s",
-                      "peak": MFMA_F32_PEAK_TFLOPS, "frac": round(exact_tflops / MFMA_F32_PEAK_TFLOPS, 4)},
+                      "peak": MFMA_F32_PEAK_TFLOPS, "frac": round(exact_tflops / MFMA_F32_PEAK_TFLOPS, 4),
+                      "logits_launch": {"kernel": "tinyblas_mfma<true, false> (128256x4096, n=512)",
+                                        "avg_launch_us": round(exact_lo_ms * 1e3, 1), "flops": lo_flops,
+                                        "achieved": round(ex_lo_tf, 2), "unit": "TFLOP/s",
+                                        "peak": MFMA_F32_PEAK_TFLOPS,
+                                        "frac": round(ex_lo_tf / MFMA_F32_PEAK_TFLOPS, 4)}},
             "mfma": {"kernel": "mfma_fast (fp16 MFMA)", "bound": "mfma",
                      "achieved": round(mfma_tflops, 1), "unit": "TFLOP/s",
-                     "peak": MFMA_F16_PEAK_TFLOPS, "frac": round(mfma_tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+                     "peak": MFMA_F16_PEAK_TFLOPS, "frac": round(mfma_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     "logits_launch": {"kernel": "mfma_fast<256, 256, 2, 4, 2> (128256x4096, n=512)",
+                                       "avg_launch_us": round(mfma_lo_ms * 1e3, 1), "flops": lo_flops,
+                                       "achieved": round(mf_lo_tf, 1), "unit": "TFLOP/s",
+                                       "peak": MFMA_F16_PEAK_TFLOPS,
+                                       "frac": round(mf_lo_tf / MFMA_F16_PEAK_TFLOPS, 4)}},
         },
+        "c1_576x576": c1,
         "smollm2_135m": small,
-        "next_rows": dict({"get_rows_512x4096": {"avg_us": round(gr_us, 2), "bytes": gr_bytes,
-                                                 "GB_s": round(gr_bytes / (gr_us * 1e-6) / 1e9, 1)}}, **attn),
+        "next_rows": dict({"get_rows_512x4096": {"avg_us": round(gr_ms * 1e3, 2), "bytes": gr_bytes,
+                                                 "GB_s": round(gr_bytes / (gr_ms * 1e-3) / 1e9, 1)}}, **attn),
         "setup_s": round(setup_s, 1),
     }
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(host_w, dec, dec_k, S, N, args.cpu_sample_rows, value)
+        out["cpu_baseline"] = cpu_baseline(host_w, dec, dec_k, S, N, args.cpu_sample_rows, value, args.dist)
 
     print(json.dumps(out), flush=True)
+
+
+def per_launch_ms(torch, ev, fn, n):
+    """n calls of fn, each between its own pair of HIP events on the current
+    stream; the list of durations in ms."""
+    pairs = [(ev(), ev()) for _ in range(n)]
+    for a, b in pairs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+def back_to_back_ms(torch, ev, fn, n):
+    """Average ms per call of n calls issued back to back between two HIP
+    events on the current stream."""
+    fn()
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def stats(vals):
+    """median, p10, p90 (nearest rank) and count of a list of durations (the
+    unit of the list, rounded to 4 decimals)."""
+    v = sorted(vals)
+    q = lambda f: v[min(len(v) - 1, max(0, int(round(f * (len(v) - 1)))))]  # noqa: E731
+    return {"median": round(q(0.5), 4), "p10": round(q(0.1), 4), "p90": round(q(0.9), 4), "n": len(v)}
+
+
+def c1_leg(f16wm, torch, np, synth, dev, ev, n):
+    """The 576x576 weight (seed 0) at n = 1 (vec_dot) and n = 3 (tinyBLAS),
+    f32 columns rounded inside the launch: per-launch times (launch-bound)."""
+    w, a = synth.c1()
+    wd = torch.from_numpy(w.view(np.int16)).to(dev).view(torch.float16)
+    ad = torch.from_numpy(a).to(dev)
+    o1 = torch.empty(576, dtype=torch.float32, device=dev)
+    o3 = torch.empty((3, 576), dtype=torch.float32, device=dev)
+    t1 = per_launch_ms(torch, ev, lambda: f16wm.mat_vec(wd, ad[0], o1), n)
+    t3 = per_launch_ms(torch, ev, lambda: f16wm.mat_mul(wd, ad, o3), n)
+    return {"n1_mat_vec_us": {k: (round(v * 1e3, 2) if k != "n" else v) for k, v in stats(t1).items()},
+            "n3_mat_mul_us": {k: (round(v * 1e3, 2) if k != "n" else v) for k, v in stats(t3).items()}}
 
 
 def smollm2_135m_leg(f16wm, torch, np, synth, dev, reps):
@@ -408,6 +483,13 @@ def smollm2_135m_leg(f16wm, torch, np, synth, dev, reps):
         f16wm.to_f16(XN["qkv"], AN["qkv"])
         mm([W[(0, "logits")]], AN["qkv"], [ON["logits"]])
 
+    # the same decode products as tables (f16wm_mat_vec_table), one per weight
+    # copy: 181 short-row products (two launches of at most 96) and 30 staged
+    # ones (one launch)
+    src = {"q": "qkv", "k": "qkv", "v": "qkv", "o": "o", "gate": "gateup", "up": "gateup", "down": "down"}
+    tables = {id(W): f16wm.VecTable([(W[(l, m)], X1[(l, src[m])], O1[(l, m)]) for l in range(L) for m in S] +
+                                    [(W[(0, "logits")], X1["logits"], O1["logits"])]) for W in Wc}
+
     dec_launches = 4 * L + 1
     dec_bytes = sum(2 * S[m][0] * S[m][1] + 4 * S[m][0] for m in S) * L + sum(4 * k for _, _, k in groups) * L \
         + 2 * LOG[0] * LOG[1] + 4 * LOG[0] + 4 * LOG[1]
@@ -419,6 +501,7 @@ def smollm2_135m_leg(f16wm, torch, np, synth, dev, reps):
     res = {}
     for name, fn, outs in (
             ("decode_step", lambda W: decode(W), [O1["logits"], O1[(L - 1, "down")], O1[(0, "q")]]),
+            ("decode_table", lambda W: tables[id(W)](), [O1["logits"], O1[(L - 1, "down")], O1[(0, "q")]]),
             ("prefill_exact", lambda W: prefill(W, False), [ON["logits"], ON[(L - 1, "down")], ON[(0, "k")]]),
             ("prefill_mfma", lambda W: prefill(W, True), [ON["logits"], ON[(L - 1, "down")], ON[(0, "k")]])):
         for _ in range(2):
@@ -458,10 +541,13 @@ def smollm2_135m_leg(f16wm, torch, np, synth, dev, reps):
         graph_us = e0.elapsed_time(e1) * 1e3 / (reps * COPIES)
         del graph
         r = {"graph_us": round(graph_us, 2), "eager_us": round(eager_us, 2), "graph_bits_equal_eager": same}
-        if name == "decode_step":
-            r.update({"launches": dec_launches, "bytes": dec_bytes,
+        if name.startswith("decode"):
+            r.update({"launches": dec_launches if name == "decode_step" else 3, "bytes": dec_bytes,
                       "GB_s": round(dec_bytes / (graph_us * 1e-6) / 1e9, 1),
                       "steps_per_s": round(1e6 / graph_us, 1)})
+            if name == "decode_table":
+                r["what"] = ("the step's 211 products as one f16wm_mat_vec_table call (independent products: "
+                             "every column is a seeded input; a model's layers depend on each other)")
         else:
             r.update({"launches": 2 * (4 * L + 1), "flops": pre_flops,
                       "TFLOP_s": round(pre_flops / (graph_us * 1e-6) / 1e12, 2)})
@@ -538,14 +624,32 @@ def attention_helpers_leg(f16wm, torch, np, synth, dev, ev):
     }
 
 
-def cpu_baseline(host_w, dec, dec_k, S, N, sample_div, gpu_value):
+def host_cpus():
+    """What the host offers: os.cpu_count(), the CPUs this process may run
+    on, and `nproc`."""
+    import subprocess
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = None
+    try:
+        nproc = int(subprocess.run(["nproc"], capture_output=True, text=True, timeout=10).stdout.strip())
+    except Exception:  # noqa: BLE001 - reported as unknown
+        nproc = None
+    return {"os_cpu_count": os.cpu_count(), "affinity": aff, "nproc": nproc}
+
+
+def cpu_baseline(host_w, dec, dec_k, S, N, sample_div, gpu_value, ndist):
     """The oracle as it stands, on the host cores: the full decode GEMV set
     (same inputs), repeated until about 5 s have passed, and the exact
     n = 512 products on the first rows/N rows of every matrix (about 8 s at
-    N = 4 on 16 cores)."""
+    N = 4 on 16 cores), both on the CPUs this process may use up to 16 (one
+    GPU's share of a shared host); and the 576x576 case on one thread,
+    ndist times (median, p10, p90)."""
     import numpy as np
 
     import oracle
+    import synth
 
     orc = oracle.default()
     T = cpu_threads()
@@ -563,7 +667,6 @@ def cpu_baseline(host_w, dec, dec_k, S, N, sample_div, gpu_value):
         reps += 1
     dt_gemv = time.perf_counter() - t
     nbytes = reps * step_bytes
-    import synth
     pre = synth.activation(synth.CFG_8B_PREFILL, 0, 0, N, 14336)
     flops = 0
     t = time.perf_counter()
@@ -573,15 +676,32 @@ def cpu_baseline(host_w, dec, dec_k, S, N, sample_div, gpu_value):
         orc.mat_mul(w[:rows], orc.to_f16(pre[:, :k]), threads=T)
         flops += 2 * rows * k * N
     dt_mm = time.perf_counter() - t
+    # the 576x576 case on one thread
+    w1, a1 = synth.c1()
+    t1, t3 = [], []
+    for _ in range(ndist):
+        t = time.perf_counter()
+        a16 = orc.to_f16(a1)
+        orc.mat_vec(w1, a16[0], threads=1)
+        t1.append((time.perf_counter() - t) * 1e6)
+        t = time.perf_counter()
+        orc.mat_mul(w1, orc.to_f16(a1), threads=1)
+        t3.append((time.perf_counter() - t) * 1e6)
+    c1_bytes = 2 * 576 * 576 + 4 * 576 + 4 * 576
+    us = lambda v: {k: (round(x, 1) if k != "n" else x) for k, x in stats(v).items()}  # noqa: E731
     return {
         "value": round(nbytes / dt_gemv / 1e9, 3),
         "unit": "GB/s",
         "cores": T,
         "kind": "oracle",
         "sample": "decode: the full 8B GEMV set %d times (%d bytes each, %.2f s); prefill exact: the first 1/%d "
-                  "of the rows of every matrix at n=512 (%.3g FLOP, %.2f s)" % (reps, step_bytes, dt_gemv, sample_div,
-                                                                              flops, dt_mm),
+                  "of the rows of every matrix at n=512 (%.3g FLOP, %.2f s); 576x576 at n=1 and n=3 on one "
+                  "thread, %d times each" % (reps, step_bytes, dt_gemv, sample_div, flops, dt_mm, ndist),
+        "host": dict(host_cpus(), threads_used=T,
+                     note="oracle threads = the CPUs this process may use, at most 16 (one GPU's share)"),
         "gemm_exact_tflops": round(flops / dt_mm / 1e12, 5),
+        "c1_576x576_single_thread": {"n1_mat_vec_us": us(t1), "n3_mat_mul_us": us(t3),
+                                     "n1_GB_s_median": round(c1_bytes / stats(t1)["median"] / 1e3, 3)},
         "gpu_over_cpu": round(gpu_value / (nbytes / dt_gemv / 1e9), 1),
     }
 
