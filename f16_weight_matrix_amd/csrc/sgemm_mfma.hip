@@ -27,8 +27,9 @@
 //    one 32 x 32 tile x four instructions x 32 accumulators = 128
 //    accumulators, and two blocks share a CU (two waves per SIMD, at most
 //    256 registers each).  Per step a wave issues four MFMAs from two
-//    16-byte LDS reads, read one step ahead so their latency hides behind
-//    the matrix core.  Measured against 64 x 128 blocks with one wave per
+//    16-byte LDS reads, read two steps ahead so their latency hides behind
+//    the matrix core (one step ahead was 0.4-3 % slower per shape).
+//    Measured against 64 x 128 blocks with one wave per
 //    SIMD (32 x 64 per wave, 256 accumulators): 11 % faster on the 8B-shaped
 //    set at n = 512 (126 instead of 113 TFLOP/s on the large products) and
 //    34 % faster on the 135M-shaped set, whose small matrices then give
@@ -331,15 +332,14 @@ __global__ __launch_bounds__(256, 2) void tinyblas_mfma(GemmTable g, int64_t k, 
         char *nwl = lds + ((st + 1) & 1) * (kWBuf + kXBuf);
         char *nxl = nwl + kWBuf;
         const int64_t kfetch = (st + 2) * kKS;
-        // operands one step ahead of the MFMAs that use them
-        f32x4 wa, x0;
+        // operands two steps ahead of the MFMAs that use them
+        f32x4 wa, x0, wa1, x01;
         read_step(wl, xl, 0, h, wrow, xcol, wa, x0);
+        read_step(wl, xl, 1, h, wrow, xcol, wa1, x01);
         static_for<0, kSteps>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             f32x4 nwa, nx0;
-            if constexpr (t + 1 < kSteps) read_step(wl, xl, t + 1, h, wrow, xcol, nwa, nx0);
-            // keep the reads ahead of this step's MFMAs (their latency then
-            // hides behind the matrix core instead of stalling it)
+            if constexpr (t + 2 < kSteps) read_step(wl, xl, t + 2, h, wrow, xcol, nwa, nx0);
             __builtin_amdgcn_sched_barrier(0);
             static_for<0, 4>([&](auto pc) {
                 constexpr int p = decltype(pc)::value;
@@ -353,8 +353,12 @@ __global__ __launch_bounds__(256, 2) void tinyblas_mfma(GemmTable g, int64_t k, 
                 }
             });
             if constexpr (t + 1 < kSteps) {
-                wa = nwa;
-                x0 = nx0;
+                wa = wa1;
+                x0 = x01;
+            }
+            if constexpr (t + 2 < kSteps) {
+                wa1 = nwa;
+                x01 = nx0;
             }
         });
         // buffer (st + 1) % 2 is complete, and every wave is done reading
