@@ -43,14 +43,6 @@
 namespace f16wm {
 namespace {
 
-__device__ __forceinline__ void fma8(float (&acc)[8], u32x4 w, u32x4 a)
-{
-    const half8 wh = __builtin_bit_cast(half8, w);
-    const half8 ah = __builtin_bit_cast(half8, a);
-#pragma unroll
-    for (int l = 0; l < 8; l++) acc[l] = __builtin_fmaf((float)wh[l], (float)ah[l], acc[l]);
-}
-
 __device__ __forceinline__ int find_matrix(const RowTable &t, int64_t g)
 {
     int m = 0;
@@ -67,21 +59,6 @@ __device__ __forceinline__ uint16_t act16(const void *a, int64_t i)
 {
     if (kF32) return rne_f16(static_cast<const float *>(a)[i]);
     return static_cast<const uint16_t *>(a)[i];
-}
-
-// Eight consecutive activation elements (16-byte aligned) as f16 bit patterns.
-template <bool kF32>
-__device__ __forceinline__ u32x4 act8(const void *a, int64_t i)
-{
-    if (!kF32) return *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a) + i);
-    const float4 p = *reinterpret_cast<const float4 *>(static_cast<const float *>(a) + i);
-    const float4 q = *reinterpret_cast<const float4 *>(static_cast<const float *>(a) + i + 4);
-    u32x4 o;
-    o.x = (uint32_t)rne_f16(p.x) | ((uint32_t)rne_f16(p.y) << 16);
-    o.y = (uint32_t)rne_f16(p.z) | ((uint32_t)rne_f16(p.w) << 16);
-    o.z = (uint32_t)rne_f16(q.x) | ((uint32_t)rne_f16(q.y) << 16);
-    o.w = (uint32_t)rne_f16(q.z) | ((uint32_t)rne_f16(q.w) << 16);
-    return o;
 }
 
 // The k % 32 tail in binary64, ascending, onto the f32 tree result.
