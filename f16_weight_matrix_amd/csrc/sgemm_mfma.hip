@@ -38,10 +38,13 @@
 //    the operands already widened to f32 (exactly, once per element and
 //    block): widening inside the step loop would put 24 conversions between
 //    every 16 MFMAs and keep the matrix core a quarter idle.
-//  - Global loads run a stage ahead of their stash and two ahead of their
-//    MFMAs: while stage st computes, stage st + 1's chunks (in registers) are
-//    widened and written to the other buffer between the MFMAs, a few at a
-//    time, and each register is refilled with its chunk of stage st + 2.
+//  - Global loads run two stages ahead of their stash and three ahead of
+//    their MFMAs: while stage st computes, stage st + 1's chunks (in one of
+//    two register sets, one per stage parity) are widened and written to
+//    the other buffer between the MFMAs, a few at a time, and each register
+//    is refilled with its chunk of stage st + 3 (one stage of lead, with a
+//    single register set, was 1-2 % slower on the large products and 20 %
+//    on q/k/v, whose second round of blocks runs one block per CU).
 //    Aligned operands use raw buffer loads whose resource covers only this
 //    tile; an offset past its end reads zero, so rows past the matrix,
 //    columns past n and chunks past k (k % 8 == 0: a chunk is all in or all
@@ -318,20 +321,24 @@ __global__ __launch_bounds__(256, 2) void tinyblas_mfma(GemmTable g, int64_t k, 
     // Pipeline: during stage st the MFMAs read LDS buffer st % 2, the chunks
     // of stage st + 1 (in registers) are stashed into buffer (st + 1) % 2
     // between them, and each register, once stashed, is reloaded with its
-    // chunk of stage st + 2, which so has a whole stage to arrive.  Chunks
-    // past k are zero, so the last stages need no special case.
+    // chunk of stage st + 3: two register sets, one per stage parity, so a
+    // chunk has two whole stages to arrive.  Chunks past k are zero, so the
+    // last stages need no special case.
     const int64_t nstages = (k + kKS - 1) / kKS;
-    u32x4 wreg[kWPT], xreg[kXPT][2];
-    fetch_stage<kBuf, kF32>(wreg, xreg, src, 0, tid);
-    stash_stage<kF32>(lds, lds + kWBuf, wreg, xreg, tid);
-    fetch_stage<kBuf, kF32>(wreg, xreg, src, kKS, tid);
+    u32x4 wr0[kWPT], xr0[kXPT][2], wr1[kWPT], xr1[kXPT][2];
+    fetch_stage<kBuf, kF32>(wr0, xr0, src, 0, tid);
+    stash_stage<kF32>(lds, lds + kWBuf, wr0, xr0, tid);
+    fetch_stage<kBuf, kF32>(wr1, xr1, src, kKS, tid);       // stage 1: set 1
+    fetch_stage<kBuf, kF32>(wr0, xr0, src, 2 * kKS, tid);   // stage 2: set 0
     __syncthreads();
-    for (int64_t st = 0; st < nstages; st++) {
+    // Stage st, whose next stage waits in (wreg, xreg): the set of parity
+    // (st + 1) % 2.
+    auto stage = [&](int64_t st, u32x4(&wreg)[kWPT], u32x4(&xreg)[kXPT][2]) {
         const char *wl = lds + (st & 1) * (kWBuf + kXBuf);
         const char *xl = wl + kWBuf;
         char *nwl = lds + ((st + 1) & 1) * (kWBuf + kXBuf);
         char *nxl = nwl + kWBuf;
-        const int64_t kfetch = (st + 2) * kKS;
+        const int64_t kfetch = (st + 3) * kKS;
         // operands two steps ahead of the MFMAs that use them
         f32x4 wa, x0, wa1, x01;
         read_step(wl, xl, 0, h, wrow, xcol, wa, x0);
@@ -364,7 +371,13 @@ __global__ __launch_bounds__(256, 2) void tinyblas_mfma(GemmTable g, int64_t k, 
         // buffer (st + 1) % 2 is complete, and every wave is done reading
         // buffer st % 2, which stage st + 1 overwrites
         __syncthreads();
+    };
+    int64_t st = 0;
+    for (; st + 1 < nstages; st += 2) {
+        stage(st, wr1, xr1);
+        stage(st + 1, wr0, xr0);
     }
+    if (st < nstages) stage(st, wr1, xr1);
 
     // hsum in the page's order, then out[c*rows + r] for 4 consecutive rows.
     // Register v (< 16) of instruction p holds chain lane p and v + 16 lane
