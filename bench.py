@@ -322,6 +322,7 @@ def main():
         "phases_ms": {"decode_table": round(dec_table_avg, 4),
                       "prefill_exact": round(exact_avg, 4), "prefill_mfma": round(mfma_avg, 4)},
         "decode_table_launch_ms": stats(table_ms),
+        "decode_tokens_per_s_equivalent": round(1e3 / dec_table_avg, 1),
         "decode_sequence": {
             "what": "the same eight products as five dependent launches (Q/K/V grouped, O, gate/up grouped, down, "
                     "logits), as a model's layer issues them",
@@ -544,7 +545,9 @@ def smollm2_135m_leg(f16wm, torch, np, synth, dev, reps):
         if name.startswith("decode"):
             r.update({"launches": dec_launches if name == "decode_step" else 3, "bytes": dec_bytes,
                       "GB_s": round(dec_bytes / (graph_us * 1e-6) / 1e9, 1),
-                      "steps_per_s": round(1e6 / graph_us, 1)})
+                      "steps_per_s": round(1e6 / graph_us, 1),
+                      "tokens_per_s_equivalent": round(1e6 / graph_us, 1),
+                      "tokens_per_s_note": "one decode step's weight stream per token (the products only)"})
             if name == "decode_table":
                 r["what"] = ("the step's 211 products as one f16wm_mat_vec_table call (independent products: "
                              "every column is a seeded input; a model's layers depend on each other)")
