@@ -470,17 +470,25 @@ int f16wm_mat_vec_table(const f16wm_gemv *prods, int32_t count, void *stream)
             std::vector<int> &v = cls[d][f];
             // longest rows first, so the blocks that take longest start first
             std::stable_sort(v.begin(), v.end(), [&](int x, int y) { return prods[x].k > prods[y].k; });
-            for (size_t c0 = 0; c0 < v.size(); c0 += f16wm::kTableChunk) {
+            // Chunks of at most kTableChunk products and 2^31 - 1 row tiles
+            // (the grid's limit; a product has at most 2^27 tiles of 16 rows).
+            const int64_t per = d == 1 ? f16wm::kTableRowsDirect : f16wm::kTableRowsLds;
+            size_t i = 0;
+            while (i < v.size()) {
                 f16wm::ProdTable t = {};
-                const size_t c1 = std::min(v.size(), c0 + (size_t)f16wm::kTableChunk);
-                for (size_t i = c0; i < c1; i++) {
+                int64_t tiles = 0;
+                while (i < v.size() && t.count < f16wm::kTableChunk) {
                     const f16wm_gemv &g = prods[v[i]];
+                    const int64_t pt = (g.rows + per - 1) / per;
+                    if (t.count > 0 && tiles + pt > 0x7fffffff) break;
+                    tiles += pt;
                     t.w[t.count] = g.w;
                     t.a[t.count] = g.a;
                     t.out[t.count] = g.out;
                     t.rows[t.count] = (int32_t)g.rows;
                     t.k[t.count] = (int32_t)g.k;
                     t.count++;
+                    i++;
                 }
                 const hipError_t e = f16wm::launch_vec_dot_table(t, d == 1, f == 1, (hipStream_t)stream);
                 if (e != hipSuccess) return launched(fn, e);
