@@ -755,6 +755,32 @@ def test_llama3_8b_prefill_512(orc, m):
         % (m, got.size, e, f32_accumulation_bound(k), rel, rr.size))
 
 
+@pytest.mark.parametrize("group", [("q", "k", "v"), ("gate", "up")])
+def test_llama3_8b_grouped_prefill_as_bench(orc, group):
+    """The grouped n = 512 launches the benchmark times (Q/K/V in one launch,
+    gate/up in one launch, sharing one rounded activation block), exact
+    order on every element against the oracle, and the MFMA product sampled
+    in every 64 x 64 output block."""
+    S = synth.LLAMA3_8B
+    k = S[group[0]][1]
+    acts = synth.activation(synth.CFG_8B_PREFILL, 0, 0, synth.PREFILL_N, 14336)
+    x = np.ascontiguousarray(acts[:, :k])
+    del acts
+    a16 = orc.to_f16(x)
+    ws = {m: synth.weight(synth.CFG_8B, 0, m, *S[m]) for m in group}
+    wd = [up16(ws[m]) for m in group]
+    ad = f16wm.to_f16(up32(x))                       # rounded on the GPU, as the bench does
+    assert np.array_equal(ad.view(torch.int16).cpu().numpy().view(np.uint16), a16)
+    exact = [o.cpu().numpy() for o in f16wm.mat_mul_multi(wd, ad)]
+    mfma = [o.cpu().numpy() for o in f16wm.mat_mul_mfma_multi(wd, ad)]
+    del wd, ad
+    for i, m in enumerate(group):
+        assert_bits_equal(exact[i], orc.mat_mul(ws[m], a16, threads=HOST_T), "8B grouped prefill %s" % m)
+        rr, cc = tile_samples(S[m][0], synth.PREFILL_N, 40 + i)
+        e, rel = mfma_check(orc, ws[m], a16, mfma[i], rr, cc, "8B grouped mfma %s" % m)
+        say("8B grouped %s: exact ok; mfma err %.3g rel %.3g" % (m, e, rel))
+
+
 # ------------------------------------------- decode sequences as HIP graphs
 
 def _replay_and_check(graph, outs, wants, what, eager=None, replays=3):
