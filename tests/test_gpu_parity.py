@@ -271,6 +271,48 @@ def test_shapes_and_alignment(orc, rows, k, n, woff, aoff):
                       "mat_vec %dx%d" % (rows, k))
 
 
+def test_gemv_past_the_32_bit_offset_limit(orc):
+    """A row so long (k = 2^26 + 40: 134 MB per row) that 16 rows of it pass the
+    2^31-byte offsets of the staged kernels: the launch falls back to the
+    one-lane-per-chain kernel, through f16wm_mat_vec and through a table;
+    every element against the oracle, the 8-element tail included."""
+    k = (1 << 26) + 40
+    w = synth.random_f16((86, 1), (3, k), 0.02)
+    a = synth.random_f16((86, 2), (k,))
+    want = orc.mat_vec(w, a, threads=HOST_T)
+    wd, ad = up16(w), up16(a)
+    assert_bits_equal(f16wm.mat_vec(wd, ad).cpu().numpy(), want, "mat_vec k=2^26+40")
+    outs = f16wm.mat_vec_table([(wd, ad), (wd[:1], ad)])
+    assert_bits_equal(outs[0].cpu().numpy(), want, "table k=2^26+40")
+    assert_bits_equal(outs[1].cpu().numpy(), want[:1], "table k=2^26+40, one row")
+
+
+def test_random_shapes_every_exact_kernel(orc):
+    """120 seeded random products (rows 1-700, k 1-3000, n 1-300, f16 or f32
+    activations, aligned or not): every kernel class of the exact orders on
+    shapes nobody picked, every element against the oracle."""
+    rng = np.random.default_rng(2024)
+    for case in range(120):
+        rows = int(rng.integers(1, 700))
+        k = int(rng.choice([int(rng.integers(1, 3000)), 8 * int(rng.integers(1, 375))]))
+        n = int(rng.choice([1, 2, 3, int(rng.integers(1, 300))]))
+        if rng.random() < 0.5:
+            rows = max(4, rows // 4 * 4)                 # takes_sgemm more often
+        f32 = bool(rng.random() < 0.3)
+        woff, aoff = (0, 0) if rng.random() < 0.7 else (int(rng.integers(0, 8)), int(rng.integers(0, 8)))
+        w = synth.random_f16((87, case, 1), (rows, k), 0.02)
+        if f32:
+            x = rng.standard_normal((n, k)).astype(np.float32)
+            a16 = orc.to_f16(x)
+            got = f16wm.mat_mul(up16(w, woff), up32(x, aoff)).cpu().numpy()
+        else:
+            a16 = synth.random_f16((87, case, 2), (n, k))
+            got = f16wm.mat_mul(up16(w, woff), up16(a16, aoff)).cpu().numpy()
+        assert_bits_equal(got, orc.mat_mul(w, a16, threads=HOST_T),
+                          "random case %d: rows=%d k=%d n=%d f32=%s offs=%d,%d" % (case, rows, k, n, f32, woff, aoff))
+    say("120 random exact products bit-exact")
+
+
 # ------------------------------------------------------------ grouped GEMV
 
 @pytest.mark.parametrize("shapes", [
