@@ -700,6 +700,23 @@ def test_mfma_small_shapes(orc, rows, k, n):
         % (rows, k, n, rr.size, e, f32_accumulation_bound(k), rel))
 
 
+def test_random_shapes_mfma(orc):
+    """40 seeded random MFMA products (rows 1-3000, k a multiple of 8 up to
+    5000 -- k % 64 != 0 takes the generic kernel --, n 1-600), each sampled in
+    every 64 x 64 output block against the acceptance check."""
+    rng = np.random.default_rng(2025)
+    for case in range(40):
+        rows = int(rng.integers(1, 3000))
+        k = 8 * int(rng.integers(1, 625))
+        n = int(rng.integers(1, 600))
+        w = synth.random_f16((88, case, 1), (rows, k), 0.02)
+        a = synth.random_f16((88, case, 2), (n, k))
+        got = f16wm.mat_mul_mfma(up16(w), up16(a)).cpu().numpy()
+        rr, cc = tile_samples(rows, n, 100 + case, per=4)
+        mfma_check(orc, w, a, got, rr, cc, "random mfma case %d: rows=%d k=%d n=%d" % (case, rows, k, n))
+    say("40 random MFMA products within the bounds")
+
+
 # ----------------------------------------------- full-size model shapes
 
 def test_smollm2_135m_decode_step_all_matrices(orc):
