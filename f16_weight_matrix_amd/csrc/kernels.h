@@ -95,7 +95,7 @@ hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32a
 // else rows staged in LDS.  f32act: every column is f32, rounded in the
 // kernel exactly as launch_to_f16 rounds it.  The launcher fills tile0 and
 // fails (hipErrorInvalidConfiguration) past 2^31 - 1 row tiles.
-constexpr int64_t kDirectMaxKTable = 640;
+constexpr int64_t kDirectMaxKTable = 576;
 constexpr int kTableRowsDirect = 16;   // rows per block, direct kernel
 constexpr int kTableRowsLds = 16;      // rows per block, LDS kernel
 hipError_t launch_vec_dot_table(ProdTable t, bool direct, bool f32act, hipStream_t stream);

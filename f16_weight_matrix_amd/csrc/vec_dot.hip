@@ -21,7 +21,7 @@
 // and c ^ b, across lanes when b >= CPL and inside a lane otherwise
 // (vec_dot_order.h).  Every layout holds the same 32 chains and applies the
 // same adds, so all give the same bits:
-//   vec_dot_direct (k <= 640, k % 8 == 0, 16-byte alignment): 4 lanes per
+//   vec_dot_direct (k <= 576, k % 8 == 0, 16-byte alignment): 4 lanes per
 //         row, each loading the 16 bytes W[r][32t + 8q .. +7] of its chains
 //         per step straight into registers.
 //   vec_dot_lds (k % 8 == 0, 16-byte alignment): 16 or 32 lanes per row,
@@ -179,14 +179,20 @@ __device__ __forceinline__ void lds_tile(const uint16_t *__restrict__ wm, int64_
     const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wm + r0 * k, vrows * k * 2);
     const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(a, k * ESZ);
 
-    // Byte offsets of this thread's stage units in stage 0: unit f = row
-    // f / U, 16 bytes at element 8 * (f % U); stage s adds 2 * SC * s.
+    // This thread's stage units: unit p is 16 bytes of row urow(p) at
+    // element 8 * ucol(p); stage s adds 2 * SC * s.  kWhole: each wave stages
+    // exactly the R / 4 rows it multiplies (rows rho = tid / LPR of its 64
+    // threads), so no other wave reads what it writes and a stage needs only
+    // the wave's own LDS wait, no block barrier (the shared column is in LDS
+    // before the loop).  Otherwise the 256 threads split each row's units
+    // and the per-stage activation, and every stage ends with a barrier.
+    auto urow = [&](int p) {
+        return kWhole ? (tid >> 6) * (C::R / 4) + (p * 64 + (tid & 63)) / C::U : (p * 256 + tid) / C::U;
+    };
+    auto ucol = [&](int p) { return kWhole ? (p * 64 + (tid & 63)) % C::U : (p * 256 + tid) % C::U; };
     int woff[C::UPT];
 #pragma unroll
-    for (int p = 0; p < C::UPT; p++) {
-        const int f = p * 256 + tid;
-        woff[p] = (int)((f / C::U) * k * 2 + 16 * (f % C::U));
-    }
+    for (int p = 0; p < C::UPT; p++) woff[p] = (int)(urow(p) * k * 2 + 16 * ucol(p));
     const bool act_loader = tid < C::U;
     const int aoff = act_loader ? 8 * tid * ESZ : kPastEnd;
 
@@ -210,10 +216,8 @@ __device__ __forceinline__ void lds_tile(const uint16_t *__restrict__ wm, int64_
     auto stash = [&](int set, int buf) {
         unsigned char *base = lds + buf * BUF;
 #pragma unroll
-        for (int p = 0; p < C::UPT; p++) {
-            const int f = p * 256 + tid;
-            *reinterpret_cast<u32x4 *>(base + (f / C::U) * C::ROWB + 16 * (f % C::U)) = wreg[set][p];
-        }
+        for (int p = 0; p < C::UPT; p++)
+            *reinterpret_cast<u32x4 *>(base + urow(p) * C::ROWB + 16 * ucol(p)) = wreg[set][p];
         if (!kWhole && act_loader)
             *reinterpret_cast<u32x4 *>(base + C::WBYTES + 16 * tid) = round8<kF32>(areg[set]);
     };
@@ -274,8 +278,12 @@ __device__ __forceinline__ void lds_tile(const uint16_t *__restrict__ wm, int64_
     // Stage s sits in LDS buffer s % 2 and came through register set s % D.
     // The loop runs a whole number of D-stage rounds; the stages past the
     // last only load zeros and skip the multiply, so every round issues the
-    // same loads.  Plain barriers: each wave's own LDS writes are complete
-    // (lgkmcnt(0)) before it arrives, and nothing else needs to drain.
+    // same loads.  A wave's LDS operations execute in order, so once its
+    // writes of stage s + 1 are complete (lgkmcnt(0)) it may read them, and
+    // its later writes into buffer s % 2 follow its reads of stage s.  With
+    // rows shared between waves (not kWhole) a plain barrier follows: each
+    // wave's own LDS writes are complete before it arrives, and nothing else
+    // needs to drain.
     const int64_t rounds = (nstages + D - 1) / D;
     for (int64_t s0 = 0; s0 < rounds * D; s0 += D) {
 #pragma unroll
@@ -284,7 +292,10 @@ __device__ __forceinline__ void lds_tile(const uint16_t *__restrict__ wm, int64_
             fetch(s + D, d);                     // set d is free: stage s is in LDS
             if (s < nstages) compute(s);
             stash((d + 1) % D, (int)((s + 1) & 1));
-            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (kWhole)
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            else
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         }
     }
 
@@ -338,44 +349,58 @@ __global__ __launch_bounds__(256) void vec_dot_lds_table(ProdTable t)
 }
 
 // Short rows (k <= kDirectMaxK, k % 8 == 0, 16-byte aligned): no staging.
-// Four lanes per row, lane j owning chains 8j .. 8j + 7 (the 8 elements of
-// one 16-byte piece of each step); every weight step of the row is loaded
-// straight into registers before the first is used, so the whole row arrives
-// in one memory round trip, while the block rounds the activation column
-// into LDS.  Chains, tree, tail and store as in vec_dot_lds.  For the
-// many small matrices of a small model's decode step, where a launch is a
-// few round trips long.
-constexpr int kDirectMaxK = 640;              // 20 steps of 32
+// A one-wave block takes 16 consecutive rows of one matrix, four lanes per
+// row, lane j owning chains 8j .. 8j + 7 (the 8 elements of one 16-byte
+// piece of each step).  Every load is issued up front: first the activation
+// column, then every weight step of the row, straight into registers, so the
+// whole row arrives in one memory round trip and the column is rounded into
+// LDS while the weights are still in flight.  Chains, tree, tail and store as
+// in vec_dot_lds.  For the many small matrices of a small model's decode step,
+// where a launch is a few round trips long.
+constexpr int kDirectMaxK = 576;              // 18 steps of 32
 constexpr int kDirectRows = 16;               // rows per one-wave block
 static_assert(kDirectMaxK == kDirectMaxKTable && kDirectRows == kTableRowsDirect, "table launcher's view");
 static_assert(LdsCfg<16>::R == kTableRowsLds, "table launcher's view");
 
-// direct_rows: this lane's row wrow (valid lanes) against the column a, the
-// result to *dst; the block's 64 threads hold 16 rows (one per lane quad) and
-// share `actl` (kDirectMaxK halves of LDS) for the rounded column.
+// direct_tile: rows 0 .. vrows - 1 of w0 (a matrix with k columns, from its
+// row r0), lane quad q = threadIdx.x / 4 taking row q, against the column a;
+// row q's result to dst[q].  The loads go through buffer resources that end
+// at the tile's last row and the column's last element, and steps past k
+// read from past the end: all of them read zero without memory traffic, so
+// every lane issues the same loads with no branch, and the wait for the
+// column (issued first) leaves the weight loads in flight.  The block's 64
+// threads share `actl` (kDirectMaxK halves of LDS) for the rounded column.
 template <bool kF32>
-__device__ __forceinline__ void direct_rows(unsigned char *actl, const uint16_t *__restrict__ wrow, bool valid,
+__device__ __forceinline__ void direct_tile(unsigned char *actl, const uint16_t *__restrict__ w0, int vrows,
                                             int64_t k, const void *__restrict__ a, float *__restrict__ dst)
 {
     constexpr int MAXS = kDirectMaxK / 32;
+    constexpr int ESZ = kF32 ? 4 : 2;
+    constexpr int NR = (kDirectMaxK / 8 + 63) / 64;   // column rounds of 64 threads x 8 elements
     const int tid = threadIdx.x;
-    const int j = tid & 3;
+    const int q = tid >> 2, j = tid & 3;
     const int nsteps = (int)(k >> 5);
+    const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(a, k * ESZ);
+    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(w0, vrows * k * 2);
 
+    u32x4 raw[NR][2];
+#pragma unroll
+    for (int r = 0; r < NR; r++) {
+        const int off = (64 * r + tid) * 8 * ESZ;
+        raw[r][0] = __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0);
+        if (kF32) raw[r][1] = __builtin_amdgcn_raw_buffer_load_b128(ar, off + 16, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep them ahead of the weight loads
+    const int wbase = (int)(q * k * 2) + 16 * j;
     u32x4 wv[MAXS];
 #pragma unroll
     for (int s = 0; s < MAXS; s++)
-        if (valid && s < nsteps) wv[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow + 32 * s + 8 * j));
+        wv[s] = __builtin_amdgcn_raw_buffer_load_b128(wr, s < nsteps ? wbase + 64 * s : kPastEnd, 0, 2);
     // the column, rounded, 8 elements per thread and round (k % 8 == 0)
 #pragma unroll
-    for (int u0 = 0; u0 < kDirectMaxK / 8; u0 += 64) {
-        const int u = u0 + tid;
-        if (8 * u < k) {
-            u32x4 raw[2];
-            raw[0] = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a) + 8 * u * (kF32 ? 4 : 2));
-            if (kF32) raw[1] = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a) + 8 * u * 4 + 16);
-            *reinterpret_cast<u32x4 *>(actl + 16 * u) = round8<kF32>(raw);
-        }
+    for (int r = 0; r < NR; r++) {
+        const int u = 64 * r + tid;
+        if (8 * u < k) *reinterpret_cast<u32x4 *>(actl + 16 * u) = round8<kF32>(raw[r]);
     }
     __syncthreads();
 
@@ -386,26 +411,28 @@ __device__ __forceinline__ void direct_rows(unsigned char *actl, const uint16_t 
     for (int s = 0; s < MAXS; s++)
         if (s < nsteps) fma_halves<8>(acc, wv[s], *reinterpret_cast<const u32x4 *>(actl + 64 * s + 16 * j));
     float v = vec_dot_tree<8>(acc);
-    if (valid && j == 0) {
-        if (k & 31) v = add_tail<kF32>(v, wrow, a, (int64_t)nsteps * 32, k);
-        *dst = v;
+    if (q < vrows && j == 0) {
+        if (k & 31) v = add_tail<kF32>(v, w0 + q * k, a, (int64_t)nsteps * 32, k);
+        dst[q] = v;
     }
 }
 
-// Global rows 16 blockIdx.x .. + 15 of the RowTable (rows of several
-// matrices may share a block), column blockIdx.y.
+// Row tile blockIdx.x - tile0[m] of matrix m of the RowTable (16 rows of one
+// matrix), column blockIdx.y.
 template <bool kF32>
 __global__ __launch_bounds__(64) void vec_dot_direct(RowTable t, int64_t k, const void *__restrict__ a_all)
 {
     __shared__ __attribute__((aligned(16))) unsigned char actl[kDirectMaxK * 2];
     const int64_t col = blockIdx.y;
-    const void *a = static_cast<const char *>(a_all) + col * k * (kF32 ? 4 : 2);
-    const int64_t g = (int64_t)blockIdx.x * kDirectRows + (threadIdx.x >> 2);
-    const bool valid = g < t.row0[t.count];
-    const int m = find_matrix(t, valid ? g : 0);
-    const int64_t r = valid ? g - t.row0[m] : 0;
+    int m = 0;
+#pragma unroll
+    for (int i = 1; i < F16WM_MAX_MULTI; i++)
+        if (i < t.count && (int64_t)blockIdx.x >= t.tile0[i]) m = i;
     const int64_t rows_m = t.row0[m + 1] - t.row0[m];
-    direct_rows<kF32>(actl, t.w[m] + r * k, valid, k, a, t.out[m] + col * rows_m + r);
+    const int64_t r0 = ((int64_t)blockIdx.x - t.tile0[m]) * kDirectRows;
+    const int vrows = (int)(rows_m - r0 < kDirectRows ? rows_m - r0 : kDirectRows);
+    direct_tile<kF32>(actl, t.w[m] + r0 * k, vrows, k, static_cast<const char *>(a_all) + col * k * (kF32 ? 4 : 2),
+                      t.out[m] + col * rows_m + r0);
 }
 
 // Rows 16 (blockIdx.x - tile0[p]) .. + 15 of product p of the table.
@@ -415,9 +442,9 @@ __global__ __launch_bounds__(64) void vec_dot_direct_table(ProdTable t)
     __shared__ __attribute__((aligned(16))) unsigned char actl[kDirectMaxK * 2];
     const int p = table_product(t, (int)blockIdx.x);
     const int64_t k = t.k[p];
-    const int64_t r = (int64_t)((int)blockIdx.x - t.tile0[p]) * kDirectRows + (threadIdx.x >> 2);
-    const bool valid = r < t.rows[p];
-    direct_rows<kF32>(actl, t.w[p] + (valid ? r : 0) * k, valid, k, t.a[p], t.out[p] + r);
+    const int64_t r0 = (int64_t)((int)blockIdx.x - t.tile0[p]) * kDirectRows;
+    const int vrows = (int)(t.rows[p] - r0 < kDirectRows ? t.rows[p] - r0 : kDirectRows);
+    direct_tile<kF32>(actl, t.w[p] + r0 * k, vrows, k, t.a[p], t.out[p] + r0);
 }
 
 constexpr int kV1Rows = 8;    // rows per 256-thread block, 32 lanes per row
@@ -533,11 +560,17 @@ hipError_t launch_vec_dot(const RowTable &t, int64_t k, const void *a, bool f32a
     // per row was never faster).
     const int lpr = vec8 && total >= 4096 ? 16 : 32;
     if (vec8 && k <= kDirectMaxK) {
-        const int64_t bx = (total + kDirectRows - 1) / kDirectRows;
+        RowTable td = t;
+        int64_t bx = 0;
+        for (int i = 0; i < t.count; i++) {
+            td.tile0[i] = bx;
+            bx += (t.row0[i + 1] - t.row0[i] + kDirectRows - 1) / kDirectRows;
+        }
+        td.tile0[t.count] = bx;
         if (bx > 0x7fffffff) return hipErrorInvalidConfiguration;
         for (int64_t c0 = 0; c0 < ncols; c0 += 65535) {
             const int64_t nc = ncols - c0 < 65535 ? ncols - c0 : 65535;
-            RowTable tc = t;
+            RowTable tc = td;
             for (int i = 0; i < t.count; i++) tc.out[i] = t.out[i] + c0 * (t.row0[i + 1] - t.row0[i]);
             const void *ac = static_cast<const char *>(a) + c0 * k * (f32act ? 4 : 2);
             if (f32act)

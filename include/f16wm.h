@@ -128,7 +128,7 @@ typedef struct {
  * every product of a decode step whose columns are already known, or the
  * same layer for several sequences.
  * Launches: products with k % 8 == 0 and 16-byte aligned w and a run in one
- * launch per kernel class (k <= 640: rows in registers; longer rows: staged
+ * launch per kernel class (k <= 576: rows in registers; longer rows: staged
  * in LDS; f16 or f32 columns) and per 96 products of a class, longest k
  * first; any other product takes its own f16wm_mat_vec launch.  Nothing runs
  * in between, so the products may not depend on each other: every output

@@ -328,7 +328,7 @@ def test_random_shapes_every_exact_kernel(orc):
 def test_mat_vec_multi(orc, shapes):
     """Grouped GEMVs, including row tiles that straddle two matrices and
     k % 32 tails for the 16-lane kernel (4096 rows or more), and ragged
-    groups for the short-row kernel (k <= 640)."""
+    groups for the short-row kernel (k <= 576)."""
     k = shapes[0][1]
     ws = [synth.random_f16((21, i, r, k), (r, k), 0.02) for i, (r, _) in enumerate(shapes)]
     a = synth.random_f16((22, k), (k,))
@@ -995,7 +995,7 @@ def _table_case(orc, seed, rows, k, f32, off=0):
 
 def test_mat_vec_table_every_kernel_class(orc):
     """One f16wm_mat_vec_table call over 230 products of every kind: short
-    rows (k <= 640, registers) and staged rows (k up to 16384 with the whole
+    rows (k <= 576, registers) and staged rows (k up to 16384 with the whole
     column in LDS, and k = 16392 without), f16 and f32 columns (the rounding's
     edge values included), k % 32 tails, rows that leave a ragged last tile,
     empty matrices, k = 0, a shared column and a shared weight, more than 96
@@ -1005,11 +1005,11 @@ def test_mat_vec_table_every_kernel_class(orc):
     rng = np.random.default_rng(97)
     shapes = []
     for i in range(110):                     # > 96 products of the short-row f16 class
-        shapes.append((int(rng.integers(1, 70)), int(rng.choice([8, 32, 40, 576, 640])), False, 0))
+        shapes.append((int(rng.integers(1, 70)), int(rng.choice([8, 32, 40, 544, 576])), False, 0))
     for i in range(40):                      # short rows, f32 columns
         shapes.append((int(rng.integers(1, 300)), int(rng.choice([64, 200, 576])), True, 0))
     for i in range(40):                      # staged rows
-        shapes.append((int(rng.integers(1, 400)), int(rng.choice([648, 1000, 1536, 4096, 4104])), bool(i % 2), 0))
+        shapes.append((int(rng.integers(1, 400)), int(rng.choice([584, 640, 1000, 1536, 4096, 4104])), bool(i % 2), 0))
     shapes += [(4096, 14336, False, 0), (1000, 14336, True, 0), (33, 16384, False, 0), (17, 16392, True, 0),
                (70, 16392, False, 0), (0, 576, False, 0), (5, 0, False, 0), (16, 33, False, 0), (9, 100, True, 1),
                (40, 1000, False, 1), (3, 31, True, 0)]
