@@ -416,13 +416,25 @@ __global__ __launch_bounds__(256, 2) void tinyblas_mfma(GemmTable g, int64_t k, 
 // 1024 elements, one MFMA per step), so a product with few tiles runs four
 // times as many waves.  Each chain is the same sequence of FMA steps as in
 // tinyblas_mfma; the eight lanes of an element meet in LDS at the end and
-// are added in the page's order.  Operands are widened once into LDS as
-// [step][chain lane][32 rows + 1 pad] f32: a wave reads 32 consecutive
-// words per half, and the padded stride keeps the stash's ds_write_b32
-// (eight rows x eight steps per wave) free of bank conflicts.
+// are added in the page's order.  Operands go to LDS as f16 (activations
+// rounded first), each row or column's 64 halves of a stage plus one pad
+// word: a thread's 16-byte chunk is four word writes, and the 33-word row
+// stride puts the 32 rows a wave reads per step in 32 different banks.  A
+// stage's eight steps are read and widened before its first MFMA, so the
+// dependent MFMAs issue back to back, and chunks are fetched two stages
+// before they are stashed (two register sets, by stage parity).  Measured
+// against f32 operands in LDS read one step ahead with one stage of fetch
+// lead: 6-8 % faster with f16 activation blocks, 2-5 % with f32, same bits.
+// The dependent chain itself bounds these launches: with no staging at all a
+// timing copy is only 14-23 % faster, since each 32x32x1 step of one chain
+// waits for the previous one.
 constexpr int kLT = 32;                         // rows = columns per tile
-constexpr int kLG = kLT + 1;                    // floats per (step, lane) group
-constexpr int kLBuf = kSteps * 8 * kLG * 4;     // bytes of one operand buffer
+constexpr int kLG = kLT + 1;                    // words per padded 32-float group (sizes the buffers)
+constexpr int kLBuf = kSteps * 8 * kLG * 4;     // bytes per operand buffer; the end-of-tile gather needs 2 * 2 * kLBuf >= 32 KB
+// the f16 stage (32 rows of kKS / 2 + 1 words) fits an operand buffer, and
+// the end-of-tile gather (4 waves x 32 registers x 64 lanes of f32) fits the
+// block's LDS
+static_assert(kLT * (kKS / 2 + 1) * 4 <= kLBuf && 4 * 32 * 64 * 4 <= 2 * 2 * kLBuf, "LDS layout");
 // Launches of at most this many 32 x 32 tiles take tinyblas_lanes (measured
 // on the 135M-shaped products at n = 512: q/k/v, o and down, 288-480 tiles,
 // 22-29 % faster; gate/up, 1536 tiles, no faster; 2048 tiles 20 % slower).
@@ -471,45 +483,63 @@ __global__ __launch_bounds__(256) void tinyblas_lanes(GemmTable g, int64_t k, co
         cx[0] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, 0, 0);
         if constexpr (kF32) cx[1] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? xoff + 16 : xoff, 0, 0);
     };
+    // f16 operands as stored (activations rounded first): row (column) lr,
+    // halves 8 lt .. 8 lt + 7 of the stage at word offset lr * kHW + 4 lt
+    constexpr int kHW = kKS / 2 + 1;              // words per row: 64 halves + one pad word
     auto stash = [&](char *buf, const u32x4 &cw, const u32x4 (&cx)[2]) {
-        const half8 hw = __builtin_bit_cast(half8, cw);
-        const f32x4 x0 = act4<kF32>(cx, 0), x1 = act4<kF32>(cx, 1);
-        float *fw = reinterpret_cast<float *>(buf), *fx = reinterpret_cast<float *>(buf + kLBuf);
+        uint32_t *ww = reinterpret_cast<uint32_t *>(buf), *wx = reinterpret_cast<uint32_t *>(buf + kLBuf);
+        u32x4 xh;
+        if constexpr (kF32) {
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            fw[(lt * 8 + e) * kLG + lr] = (float)hw[e];
-            fx[(lt * 8 + e) * kLG + lr] = e < 4 ? x0[e] : x1[e - 4];
+            for (int e = 0; e < 4; e++) {
+                const u32x4 hp = e < 2 ? cx[0] : cx[1];
+                const int b = 2 * (e & 1);
+                xh[e] = (uint32_t)rne_f16(__uint_as_float(hp[b])) | ((uint32_t)rne_f16(__uint_as_float(hp[b + 1])) << 16);
+            }
+        } else {
+            xh = cx[0];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            ww[lr * kHW + 4 * lt + e] = cw[e];
+            wx[lr * kHW + 4 * lt + e] = xh[e];
         }
     };
 
     const int64_t nstages = (k + kKS - 1) / kKS;
-    u32x4 cw, cx[2];
-    fetch(0, cw, cx);
-    stash(lds, cw, cx);
-    fetch(kKS, cw, cx);
+    // Two register sets: set A carries the odd stages, set B the even ones
+    // (stage 0 goes straight to LDS), each fetched two stages before it is
+    // stashed.
+    u32x4 cwA, cxA[2], cwB, cxB[2];
+    fetch(0, cwA, cxA);
+    stash(lds, cwA, cxA);
+    fetch(kKS, cwA, cxA);
+    fetch(2 * kKS, cwB, cxB);
     __syncthreads();
-    for (int64_t st = 0; st < nstages; st++) {
-        const float *fw = reinterpret_cast<const float *>(lds + (st & 1) * 2 * kLBuf);
-        const float *fx = fw + kLBuf / 4;
+    auto body = [&](int64_t st, u32x4 &cw, u32x4 (&cx)[2]) {
+        const uint16_t *hw = reinterpret_cast<const uint16_t *>(lds + (st & 1) * 2 * kLBuf);
+        const uint16_t *hx = hw + kLBuf / 2;
         char *nbuf = lds + ((st + 1) & 1) * 2 * kLBuf;
-        float wa = fw[q * kLG + i], xa = fx[q * kLG + i];
+        float wv[kSteps], xv[kSteps];
 #pragma unroll
         for (int t = 0; t < kSteps; t++) {
-            float nw = 0.f, nx = 0.f;
-            if (t + 1 < kSteps) {
-                nw = fw[((t + 1) * 8 + q) * kLG + i];
-                nx = fx[((t + 1) * 8 + q) * kLG + i];
-            }
-            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(wa, xa, acc, 0, 0, 0);
+            wv[t] = widen_h(hw[i * 2 * kHW + 8 * t + q]);
+            xv[t] = widen_h(hx[i * 2 * kHW + 8 * t + q]);
+        }
+#pragma unroll
+        for (int t = 0; t < kSteps; t++) {
+            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(wv[t], xv[t], acc, 0, 0, 0);
             if (t == 3) {
-                // stage st + 1 into the other buffer, then fetch st + 2
+                // stage st + 1 into the other buffer, then refill the set with st + 3
                 stash(nbuf, cw, cx);
-                fetch((st + 2) * kKS, cw, cx);
+                fetch((st + 3) * kKS, cw, cx);
             }
-            wa = nw;
-            xa = nx;
         }
         __syncthreads();
+    };
+    for (int64_t st = 0; st < nstages; st += 2) {
+        body(st, cwA, cxA);
+        if (st + 1 < nstages) body(st + 1, cwB, cxB);
     }
 
     // Gather: wave p's registers v and v + 16 are chain lanes p and p + 4.
