@@ -262,6 +262,9 @@ __global__ __launch_bounds__(kKqThreads) void kq_dma(const uint16_t *__restrict_
 }
 
 // Eight elements per thread (n % 8 == 0, 16-byte aligned arrays) or one.
+// The 16-byte accesses are nontemporal: with every array cold (rotating
+// copies) mad is 7 % and scale 16 % faster, and with one accumulator updated
+// launch after launch (hot in the cache) neither changes.
 template <bool kVec8>
 __global__ __launch_bounds__(256) void mad_kernel(uint16_t *__restrict__ acc, const uint16_t *__restrict__ v,
                                                   const float *__restrict__ w, int64_t nvec, int64_t n)
@@ -272,8 +275,8 @@ __global__ __launch_bounds__(256) void mad_kernel(uint16_t *__restrict__ acc, co
          e += (int64_t)gridDim.x * 256 * per) {
         const float wb = w[e / n];
         if (kVec8) {
-            const half8 a = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4 *>(acc + e));
-            const half8 x = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4 *>(v + e));
+            const half8 a = __builtin_bit_cast(half8, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(acc + e)));
+            const half8 x = __builtin_bit_cast(half8, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(v + e)));
             uint16_t r[8];
 #pragma unroll
             for (int i = 0; i < 8; i++) r[i] = rne_f16_of_result(__builtin_fmaf((float)x[i], wb, (float)a[i]));
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(256) void mad_kernel(uint16_t *__restrict__ acc, co
             o[1] = (uint32_t)r[2] | ((uint32_t)r[3] << 16);
             o[2] = (uint32_t)r[4] | ((uint32_t)r[5] << 16);
             o[3] = (uint32_t)r[6] | ((uint32_t)r[7] << 16);
-            *reinterpret_cast<u32x4 *>(acc + e) = o;
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(acc + e));
         } else {
             acc[e] = rne_f16_of_result(__builtin_fmaf(widen(v[e]), wb, widen(acc[e])));
         }
@@ -299,7 +302,7 @@ __global__ __launch_bounds__(256) void scale_kernel(uint16_t *__restrict__ acc, 
          e += (int64_t)gridDim.x * 256 * per) {
         const float sb = s[e / n];
         if (kVec8) {
-            const half8 a = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4 *>(acc + e));
+            const half8 a = __builtin_bit_cast(half8, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(acc + e)));
             uint16_t r[8];
 #pragma unroll
             for (int i = 0; i < 8; i++) r[i] = rne_f16_of_result((float)a[i] * sb);
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(256) void scale_kernel(uint16_t *__restrict__ acc, 
             o[1] = (uint32_t)r[2] | ((uint32_t)r[3] << 16);
             o[2] = (uint32_t)r[4] | ((uint32_t)r[5] << 16);
             o[3] = (uint32_t)r[6] | ((uint32_t)r[7] << 16);
-            *reinterpret_cast<u32x4 *>(acc + e) = o;
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(acc + e));
         } else {
             acc[e] = rne_f16_of_result(widen(acc[e]) * sb);
         }
