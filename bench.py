@@ -285,6 +285,7 @@ def main():
     ids = torch.from_numpy(np.random.default_rng(7).integers(0, S["logits"][0], N)).to(dev)
     emb = torch.empty((N, S["logits"][1]), dtype=torch.float32, device=dev)
     gr_ms = back_to_back_ms(torch, ev, lambda: f16wm.get_rows(W["logits"], ids, emb), 20)
+    gr_graph_us = graph_per_launch_us(torch, [lambda: f16wm.get_rows(W["logits"], ids, emb)] * 20, 3)
     gr_bytes = N * S["logits"][1] * (2 + 4) + N * 8
     attn = attention_helpers_leg(f16wm, torch, np, synth, dev, ev)
 
@@ -367,8 +368,11 @@ def main():
         },
         "c1_576x576": c1,
         "smollm2_135m": small,
-        "next_rows": dict({"get_rows_512x4096": {"avg_us": round(gr_ms * 1e3, 2), "bytes": gr_bytes,
-                                                 "GB_s": round(gr_bytes / (gr_ms * 1e-3) / 1e9, 1)}}, **attn),
+        "next_rows": dict({"get_rows_512x4096": {"avg_us": round(gr_ms * 1e3, 2), "graph_us": round(gr_graph_us, 2),
+                                                 "bytes": gr_bytes,
+                                                 "GB_s": round(gr_bytes / (gr_ms * 1e-3) / 1e9, 1),
+                                                 "GB_s_graph": round(gr_bytes / (gr_graph_us * 1e-6) / 1e9, 1)}},
+                          **attn),
         "setup_s": round(setup_s, 1),
     }
 
@@ -388,6 +392,30 @@ def per_launch_ms(torch, ev, fn, n):
         b.record()
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in pairs]
+
+
+def graph_per_launch_us(torch, fns, reps):
+    """The launches fns (each one call), captured once in a HIP graph and
+    replayed reps times between two HIP events: microseconds per launch.
+    GPU-side gaps between the launches are included, the host's dispatch of
+    each launch is not (short kernels would otherwise measure Python)."""
+    for fn in fns:
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in fns:
+            fn()
+    torch.cuda.synchronize()
+    g.replay()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) * 1e3 / (reps * len(fns))
 
 
 def back_to_back_ms(torch, ev, fn, n):
@@ -585,6 +613,7 @@ def attention_helpers_leg(f16wm, torch, np, synth, dev, ev):
     e1.record()
     torch.cuda.synchronize()
     kq_us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+    kq_graph_us = graph_per_launch_us(torch, [lambda kc=kc: f16wm.kq(kc, q, out) for kc in kcs], reps)
     kq_bytes = 2 * n_kv * n_kv_head * d + 2 * n_head * d + 4 * n_head * n_kv
     del kcs
     # mad / scale rotate over 48 accumulator (and V) copies, 768 MB in all, so
@@ -614,16 +643,24 @@ def attention_helpers_leg(f16wm, torch, np, synth, dev, ev):
     torch.cuda.synchronize()
     mad_us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
     scale_us = e1.elapsed_time(e2) * 1e3 / (reps * copies)
+    mad_graph_us = graph_per_launch_us(torch, [lambda acc=acc, v=v: f16wm.mad(acc, v, w) for acc, v in zip(accs, vs)], reps)
+    scale_graph_us = graph_per_launch_us(torch, [lambda acc=acc: f16wm.scale(acc, sc) for acc in accs], reps)
     del accs, vs
     mad_bytes = nvec * n * 6 + nvec * 4
     scale_bytes = nvec * n * 4 + nvec * 4
     return {
-        "kq_32768x8x128_32heads": {"avg_us": round(kq_us, 2), "bytes": kq_bytes,
-                                   "GB_s": round(kq_bytes / (kq_us * 1e-6) / 1e9, 1)},
-        "mad_32768x128": {"avg_us": round(mad_us, 2), "bytes": mad_bytes,
-                          "GB_s": round(mad_bytes / (mad_us * 1e-6) / 1e9, 1)},
-        "scale_32768x128": {"avg_us": round(scale_us, 2), "bytes": scale_bytes,
-                            "GB_s": round(scale_bytes / (scale_us * 1e-6) / 1e9, 1)},
+        "kq_32768x8x128_32heads": {"avg_us": round(kq_us, 2), "graph_us": round(kq_graph_us, 2), "bytes": kq_bytes,
+                                   "GB_s": round(kq_bytes / (kq_us * 1e-6) / 1e9, 1),
+                                   "GB_s_graph": round(kq_bytes / (kq_graph_us * 1e-6) / 1e9, 1)},
+        "mad_32768x128": {"avg_us": round(mad_us, 2), "graph_us": round(mad_graph_us, 2), "bytes": mad_bytes,
+                          "GB_s": round(mad_bytes / (mad_us * 1e-6) / 1e9, 1),
+                          "GB_s_graph": round(mad_bytes / (mad_graph_us * 1e-6) / 1e9, 1)},
+        "scale_32768x128": {"avg_us": round(scale_us, 2), "graph_us": round(scale_graph_us, 2), "bytes": scale_bytes,
+                            "GB_s": round(scale_bytes / (scale_us * 1e-6) / 1e9, 1),
+                            "GB_s_graph": round(scale_bytes / (scale_graph_us * 1e-6) / 1e9, 1)},
+        "timing_note": ("avg_us: eager launches back to back between two HIP events (the host's dispatch of each "
+                        "launch included once it is slower than the kernel); graph_us: the same launches replayed "
+                        "as one HIP graph"),
     }
 
 
