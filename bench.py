@@ -297,6 +297,7 @@ def main():
     ex_lo_tf = lo_flops / (exact_lo_ms * 1e-3) / 1e12
     mf_lo_tf = lo_flops / (mfma_lo_ms * 1e-3) / 1e12
 
+    mfma_acc = mfma_accuracy(torch, np, host_w, AN, OM, gemv_launches, S, N)
     out = {
         "metric": "F16 GEMV GB/s (n=1) and GEMM TFLOP/s (n=512), % of MI355X roofline",
         "value": round(value, 1),
@@ -364,7 +365,8 @@ def main():
                                        "avg_launch_us": round(mfma_lo_ms * 1e3, 1), "flops": lo_flops,
                                        "achieved": round(mf_lo_tf, 1), "unit": "TFLOP/s",
                                        "peak": MFMA_F16_PEAK_TFLOPS,
-                                       "frac": round(mf_lo_tf / MFMA_F16_PEAK_TFLOPS, 4)}},
+                                       "frac": round(mf_lo_tf / MFMA_F16_PEAK_TFLOPS, 4)},
+                     "accuracy": mfma_acc},
         },
         "c1_576x576": c1,
         "smollm2_135m": small,
@@ -392,6 +394,38 @@ def per_launch_ms(torch, ev, fn, n):
         b.record()
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in pairs]
+
+
+def mfma_accuracy(torch, np, host_w, AN, OM, launches, S, N, samples=1024, seed=7):
+    """The fp16 MFMA products' error, reported apart from the exact orders:
+    `samples` seeded (column, row) outputs per matrix of the last timed step
+    against an fp64 dot product of the same f16 operands (the weights as
+    drawn, the activation block as the GPU rounded it), computed here with
+    numpy.  err_over_abs_sum is |y - ref| / sum |w * a| (the acceptance
+    measure, 2e-3 allowed); max_rel_err is |y - ref| / |ref| over the
+    samples with |ref| at least 1e-2 of the samples' rms."""
+    rng = np.random.default_rng(seed)
+    e_abs = e_rel = 0.0
+    count = 0
+    for _, mats, g in launches:
+        a64 = AN[g].cpu().numpy().astype(np.float64)                    # [N][k]
+        for m in mats:
+            rows, k = S[m]
+            r = rng.integers(0, rows, samples)
+            c = rng.integers(0, N, samples)
+            y = OM[m][torch.from_numpy(c).to(OM[m].device), torch.from_numpy(r).to(OM[m].device)]
+            y = y.cpu().numpy().astype(np.float64)
+            prod = host_w[m][r].view(np.float16).astype(np.float64) * a64[c]
+            ref = prod.sum(axis=1)
+            absum = np.abs(prod).sum(axis=1)
+            err = np.abs(y - ref)
+            e_abs = max(e_abs, float((err / np.maximum(absum, 1e-300)).max()))
+            big = np.abs(ref) >= 1e-2 * np.sqrt(np.mean(ref * ref))
+            if big.any():
+                e_rel = max(e_rel, float((err[big] / np.abs(ref[big])).max()))
+            count += samples
+    return {"samples": count, "err_over_abs_sum": float("%.3g" % e_abs), "max_rel_err": float("%.3g" % e_rel),
+            "tolerance": 2e-3, "reference": "fp64 dot products of the same f16 operands (numpy, in this script)"}
 
 
 def graph_per_launch_us(torch, fns, reps):
